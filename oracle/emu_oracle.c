@@ -1,0 +1,751 @@
+/*
+ * emu_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU implementation of the emulated FP8 scaled GEMM
+ *     y = (x @ w.T) * scale_x * scale_w
+ * as the mmaemu v0.1 documentation pages describe it (user guide, FAQ,
+ * limitations, validation evidence).  Only the test suite, the package smoke
+ * check and the benchmark's cpu_baseline leg load this file's library.  It
+ * shares no code, header, table or constant with the HIP library, and it
+ * includes nothing from it.
+ *
+ * Arithmetic.  Every product and every block sum is an exact int64 integer
+ * with an explicit power-of-two exponent.  The only floating-point steps are
+ * the IEEE binary32 additions the pages name (slow-accumulation chunk adds and
+ * the split-K combination), done with the host's IEEE arithmetic
+ * (x86-64 SSE: round to nearest even, subnormals kept), and the epilogue's
+ * roundings, which are written out below from the IEEE 754 definition of
+ * round-to-nearest-even on an exact value.
+ *
+ * Readings taken where the pages are silent are marked "Reading:" and are
+ * listed in the design notes of the repository.
+ *
+ * Mutants.  Building with -DORACLE_MUTANT=n (n > 0) plants one deliberate
+ * mistake, so that the tests can show that their pins catch it.  The default
+ * build (ORACLE_MUTANT 0) is the oracle.
+ */
+#include <float.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs binary32 arithmetic evaluated in binary32 (FLT_EVAL_METHOD 0)"
+#endif
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+/* Mutant catalogue (see tests/test_oracle_mutants.py). */
+#define MUT_FLOOR_NOT_TRUNC    1  /* floor of signed terms instead of truncation toward zero */
+#define MUT_F12                2  /* 12 retained fraction bits instead of 13 */
+#define MUT_F14                3  /* 14 retained fraction bits instead of 13 */
+#define MUT_B16                4  /* 16-product blocks instead of 32 */
+#define MUT_C_NOT_IN_MAX       5  /* incoming accumulator left out of the block maximum */
+#define MUT_NORMALISED_EXP     6  /* product exponent floor(log2|p|) instead of the field sum */
+#define MUT_NEG_ZERO_BLOCK     7  /* a block that sums to zero keeps the sign of the terms */
+#define MUT_CHUNK64            8  /* slow accumulation restarts every 64 instead of 128 */
+#define MUT_REVERSED_COMBINE   9  /* split partials added in reverse order */
+#define MUT_SINGLE_ROUNDING   10  /* bf16/fp16 rounded straight from the exact product */
+#define MUT_MUL_NOT_FMA       11  /* y32 = RN32(acc*alpha) keeping the product's zero sign */
+#define MUT_NO_BLOCKSUM_TRUNC 12  /* block sum not cut back to 1+F significant bits */
+#define MUT_SUBNORMAL_EXP     13  /* subnormal inputs take exponent emin-1 instead of emin */
+#define MUT_SLOW_NO_RESTART   14  /* slow accumulation keeps chaining across chunks */
+#define MUT_SPLIT_BALANCED    15  /* k-tiles divided floor/remainder instead of ceil-contiguous */
+#define MUT_CANON_NAN         16  /* NaN output 0x7FC00000 / 0x7FC0 instead of 0x7FFFFFFF / 0x7FFF */
+#define MUT_TRANSPOSED_W      17  /* w read as [K,N] row-major instead of [N,K] */
+
+/* ------------------------------------------------------------------------ */
+/* Public constants (mirrored in oracle/__init__.py).                        */
+enum { FMT_E4M3FN = 0, FMT_E5M2 = 1 };
+enum { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
+enum { CLS_ZERO = 0, CLS_FINITE = 1, CLS_INF = 2, CLS_NAN = 3 };
+
+typedef struct {
+    int B;  /* products per block */
+    int F;  /* retained fraction bits */
+    int Q;  /* slow-accumulation chunk length */
+    int W;  /* split-K tile width */
+} oracle_profile;
+
+/* ------------------------------------------------------------------------ */
+/* FP8 decoding.
+ *
+ * The two formats are the OCP 8-bit formats that torch calls float8_e4m3fn
+ * and float8_e5m2 (user guide, section 3 "A first GEMM": E4M3 inputs clamped
+ * to +-448; validation page, "Claims and their recordings": E4M3 x E5M2 and
+ * E5M2 x E4M3 follow the same model).
+ *
+ * A finite code decodes to (-1)^s * M * 2^(e-3) with M an integer holding
+ * three fraction bits.  For a subnormal code the exponent is the format's
+ * emin, not the exponent of the leading bit: the validation page's claims
+ * table states that subnormal inputs keep exponent emin.  E5M2 has two
+ * fraction bits; its M is doubled so both formats share the 2^(e-3) scale.
+ */
+typedef struct {
+    int cls;  /* CLS_* */
+    int s;    /* sign bit */
+    int e;    /* field exponent (emin for subnormals) */
+    int M;    /* integer significand with 3 fraction bits */
+} fp8_val;
+
+static fp8_val decode_fp8(uint8_t code, int fmt)
+{
+    fp8_val v;
+    v.s = code >> 7;
+    if (fmt == FMT_E4M3FN) {
+        int ef = (code >> 3) & 15, mf = code & 7;
+        if (ef == 15 && mf == 7) { v.cls = CLS_NAN; v.e = 0; v.M = 0; return v; }
+        if (ef == 0) {
+#if ORACLE_MUTANT == MUT_SUBNORMAL_EXP
+            v.e = -7;
+#else
+            v.e = -6;  /* emin of E4M3 = 1 - bias 7 */
+#endif
+            v.M = mf;
+        } else {
+            v.e = ef - 7;
+            v.M = 8 + mf;
+        }
+    } else {
+        int ef = (code >> 2) & 31, mf = code & 3;
+        if (ef == 31) { v.cls = (mf == 0) ? CLS_INF : CLS_NAN; v.e = 0; v.M = 0; return v; }
+        if (ef == 0) {
+#if ORACLE_MUTANT == MUT_SUBNORMAL_EXP
+            v.e = -15;
+#else
+            v.e = -14;  /* emin of E5M2 = 1 - bias 15 */
+#endif
+            v.M = 2 * mf;
+        } else {
+            v.e = ef - 15;
+            v.M = 2 * (4 + mf);
+        }
+    }
+    v.cls = (v.M == 0) ? CLS_ZERO : CLS_FINITE;
+    return v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Products.
+ *
+ * A product of two finite nonzero inputs is exact: (-1)^s * P * 2^(g-6) with
+ * P = Ma*Mb (at most 225) and g = ea + eb, the sum of the field exponents.
+ * Reading: the alignment exponent of a product is this field sum, the product
+ * is never renormalised (the claims table's "subnormal inputs keep exponent
+ * emin" only has content if the exponents come from the fields).  A product
+ * with a zero factor is a zero product: it is excluded from the block maximum
+ * (validation page, claims table, first row) and contributes nothing.
+ */
+typedef struct {
+    int cls;  /* CLS_ZERO or CLS_FINITE (specials are handled separately) */
+    int s;
+    int g;
+    int P;
+} product;
+
+static int floor_log2_u64(uint64_t v)
+{
+    int l = -1;
+    while (v) { v >>= 1; l++; }
+    return l;
+}
+
+static product make_product(fp8_val a, fp8_val b)
+{
+    product p;
+    p.s = a.s ^ b.s;
+    if (a.cls != CLS_FINITE || b.cls != CLS_FINITE) {
+        p.cls = CLS_ZERO; p.g = 0; p.P = 0;
+        return p;
+    }
+    p.cls = CLS_FINITE;
+    p.P = a.M * b.M;
+    p.g = a.e + b.e;
+#if ORACLE_MUTANT == MUT_NORMALISED_EXP
+    /* exponent of the exact product's leading bit */
+    p.g = floor_log2_u64((uint64_t)p.P) - 6 + p.g;
+#endif
+    return p;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact chain state: (-1)^neg * mag * 2^q; mag == 0 means +0. */
+typedef struct {
+    int neg;
+    int64_t mag;
+    int q;
+} exact_val;
+
+static const exact_val EXACT_PLUS_ZERO = {0, 0, 0};
+
+/* floor(m * 2^sh) for m >= 0; callers keep m << sh below 2^62. */
+static int64_t scale_floor(int64_t m, int sh)
+{
+    if (sh >= 0) return m << sh;
+    if (-sh >= 63) return 0;
+    return m >> (-sh);
+}
+
+/*
+ * One block step, step(c, products) (user guide section 1; FAQ first answer;
+ * validation page, scope table row "Hopper preset" and the H100 claims table
+ * row on 32-product blocks and 13 fraction bits):
+ *
+ *  1. E is the largest alignment exponent among the nonzero products, and,
+ *     when the incoming accumulator c is nonzero, floor(log2|c|) ("c enters in
+ *     the block's alignment").  With nothing nonzero the block gives +0.
+ *  2. The quantum is 2^q with q = E - F: every term keeps F fraction bits
+ *     relative to 2^E.
+ *  3. Each term, and c, is cut to that quantum toward zero in sign-magnitude
+ *     form (claims table: "alignment, carry, sign-magnitude truncation").
+ *  4. The terms are added exactly.  A sum that is exactly zero gives +0
+ *     (scope table row "Ada instruction model": a block result that is
+ *     exactly zero or truncates to zero is +0).
+ *  5. The sum is cut toward zero to 1+F significant bits ("block sums are
+ *     truncated to 13 fraction bits"; the carry case).
+ */
+static exact_val block_step(exact_val c, const product *p, int n, int F)
+{
+    int have = 0, E = 0;
+    for (int i = 0; i < n; i++) {
+        if (p[i].cls != CLS_FINITE) continue;
+        if (!have || p[i].g > E) E = p[i].g;
+        have = 1;
+    }
+#if ORACLE_MUTANT != MUT_C_NOT_IN_MAX
+    if (c.mag != 0) {
+        int ec = c.q + floor_log2_u64((uint64_t)c.mag);
+        if (!have || ec > E) E = ec;
+        have = 1;
+    }
+#else
+    if (!have && c.mag != 0) {
+        E = c.q + floor_log2_u64((uint64_t)c.mag);
+        have = 1;
+    }
+#endif
+    if (!have) return EXACT_PLUS_ZERO;
+
+    const int q = E - F;
+    int64_t T = 0;
+    for (int i = 0; i < n; i++) {
+        if (p[i].cls != CLS_FINITE) continue;
+        /* |term| = P * 2^(g-6), measured in units of 2^q */
+        int64_t t = scale_floor(p[i].P, p[i].g - 6 - q);
+#if ORACLE_MUTANT == MUT_FLOOR_NOT_TRUNC
+        if (p[i].s) {
+            /* floor(-x) = -ceil(x) */
+            int sh = p[i].g - 6 - q;
+            int64_t exact_num = p[i].P;
+            int inexact = (sh < 0) && ((-sh >= 63) ? (exact_num != 0)
+                                                     : ((exact_num & (((int64_t)1 << -sh) - 1)) != 0));
+            t += inexact;
+        }
+#endif
+        T += p[i].s ? -t : t;
+    }
+    if (c.mag != 0) {
+#if ORACLE_MUTANT == MUT_C_NOT_IN_MAX
+        /* c taken at the block's quantum even when it does not fit */
+        int sh = c.q - q;
+        int64_t tc = (sh > 40) ? ((int64_t)1 << 60) : scale_floor(c.mag, sh);
+#else
+        int64_t tc = scale_floor(c.mag, c.q - q);
+#endif
+        T += c.neg ? -tc : tc;
+    }
+    if (T == 0) {
+#if ORACLE_MUTANT == MUT_NEG_ZERO_BLOCK
+        exact_val z = {0, 0, 0};
+        for (int i = 0; i < n; i++)
+            if (p[i].cls == CLS_FINITE) { z.neg = p[i].s; break; }
+        return z;
+#else
+        return EXACT_PLUS_ZERO;
+#endif
+    }
+    exact_val r;
+    r.neg = T < 0;
+    uint64_t mag = (uint64_t)(T < 0 ? -T : T);
+#if ORACLE_MUTANT != MUT_NO_BLOCKSUM_TRUNC
+    int L = floor_log2_u64(mag);
+    if (L > F) mag = (mag >> (L - F)) << (L - F);
+#endif
+    r.mag = (int64_t)mag;
+    r.q = q;
+    return r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Operand access. */
+typedef struct {
+    const uint8_t *x; int xfmt; int64_t ldx;
+    const uint8_t *w; int wfmt; int64_t ldw;
+    int64_t M, N, K;
+} operands;
+
+static uint8_t x_at(const operands *o, int64_t m, int64_t k) { return o->x[m * o->ldx + k]; }
+static uint8_t w_at(const operands *o, int64_t n, int64_t k)
+{
+#if ORACLE_MUTANT == MUT_TRANSPOSED_W
+    return o->w[k * o->ldw + n];
+#else
+    return o->w[n * o->ldw + k];
+#endif
+}
+
+static int effective_B(const oracle_profile *pf)
+{
+#if ORACLE_MUTANT == MUT_B16
+    (void)pf;
+    return 16;
+#else
+    return pf->B;
+#endif
+}
+
+static int effective_F(const oracle_profile *pf)
+{
+#if ORACLE_MUTANT == MUT_F12
+    (void)pf;
+    return 12;
+#elif ORACLE_MUTANT == MUT_F14
+    (void)pf;
+    return 14;
+#else
+    return pf->F;
+#endif
+}
+
+#define MAX_B 1024
+
+/*
+ * chain(kappa): c <- +0, then c <- step(c, group) for each consecutive group
+ * of B indices of [k0, k1).  The last group may be short, which is the same
+ * as padding with zero products (zeros are excluded from the maximum).
+ * Reading: blocks start at the start of each split or chunk range.
+ */
+static exact_val chain_exact(const operands *o, int64_t m, int64_t n, int64_t k0, int64_t k1,
+                             const oracle_profile *pf, exact_val c)
+{
+    const int B = effective_B(pf), F = effective_F(pf);
+    product buf[MAX_B];
+    for (int64_t kb = k0; kb < k1; kb += B) {
+        int cnt = 0;
+        for (int64_t k = kb; k < k1 && k < kb + B; k++)
+            buf[cnt++] = make_product(decode_fp8(x_at(o, m, k), o->xfmt),
+                                      decode_fp8(w_at(o, n, k), o->wfmt));
+        c = block_step(c, buf, cnt, F);
+    }
+    return c;
+}
+
+/* (-1)^neg * mag * 2^q as binary32.  Exact whenever mag has at most 24
+ * significant bits and the value is in the normal range, which holds for every
+ * chain value with F <= 23. */
+static float exact_to_f32(exact_val v)
+{
+    if (v.mag == 0) return v.neg ? -0.0f : 0.0f;  /* the oracle itself only makes +0 */
+    float f = ldexpf((float)v.mag, v.q);
+    return v.neg ? -f : f;
+}
+
+/*
+ * Slow accumulation (validation page, H100 claims table: "slow accumulation
+ * restarts every 128 elements and adds the chunk results in K order"; scope
+ * table row "Slow accumulation": per split when split).
+ * Reading: the adder is binary32 round-to-nearest-even and the running sum
+ * starts at +0; chunks start at the start of the (split) range.
+ */
+static float slow_range(const operands *o, int64_t m, int64_t n, int64_t k0, int64_t k1,
+                        const oracle_profile *pf)
+{
+#if ORACLE_MUTANT == MUT_CHUNK64
+    const int64_t Q = 64;
+#else
+    const int64_t Q = pf->Q;
+#endif
+#if ORACLE_MUTANT == MUT_SLOW_NO_RESTART
+    (void)Q;
+    return exact_to_f32(chain_exact(o, m, n, k0, k1, pf, EXACT_PLUS_ZERO));
+#else
+    float a = 0.0f;
+    for (int64_t ck = k0; ck < k1; ck += Q) {
+        int64_t ce = (ck + Q < k1) ? ck + Q : k1;
+        float r = exact_to_f32(chain_exact(o, m, n, ck, ce, pf, EXACT_PLUS_ZERO));
+        a = a + r;
+    }
+    return a;
+#endif
+}
+
+/*
+ * Split-K on the H100 PCIe profiles (validation page, scope table row
+ * "Split-K on the H100 PCIe"; H100 claims table): contiguous runs of 128-wide
+ * k-tiles, partial sums added serially; a split can hold no k-tile.
+ * Reading: nt = ceil(K/W) tiles, tps = ceil(nt/S) tiles per split, split s
+ * covers [s*tps*W, min((s+1)*tps*W, K)); an empty split gives +0; the
+ * partials are combined acc = p0, acc = RN32(acc + p_s) for s = 1..S-1.
+ */
+static void split_range(int64_t K, int S, int W, int s, int64_t *k0, int64_t *k1)
+{
+    int64_t nt = (K + W - 1) / W;
+#if ORACLE_MUTANT == MUT_SPLIT_BALANCED
+    int64_t base = nt / S, rem = nt % S;
+    int64_t t0 = s * base + (s < rem ? s : rem);
+    int64_t t1 = t0 + base + (s < rem ? 1 : 0);
+    *k0 = t0 * W;
+    *k1 = t1 * W < K ? t1 * W : K;
+#else
+    int64_t tps = (nt + S - 1) / S;
+    *k0 = (int64_t)s * tps * W;
+    int64_t e = (int64_t)(s + 1) * tps * W;
+    *k1 = e < K ? e : K;
+#endif
+    if (*k0 > K) *k0 = K;
+}
+
+static float finite_accumulator(const operands *o, int64_t m, int64_t n, int fast, int S,
+                                const oracle_profile *pf)
+{
+    float p[4096];
+    for (int s = 0; s < S; s++) {
+        int64_t k0, k1;
+        split_range(o->K, S, pf->W, s, &k0, &k1);
+        if (k0 >= k1) { p[s] = 0.0f; continue; }
+        p[s] = fast ? exact_to_f32(chain_exact(o, m, n, k0, k1, pf, EXACT_PLUS_ZERO))
+                    : slow_range(o, m, n, k0, k1, pf);
+    }
+#if ORACLE_MUTANT == MUT_REVERSED_COMBINE
+    float acc = p[S - 1];
+    for (int s = S - 2; s >= 0; s--) acc = acc + p[s];
+#else
+    float acc = p[0];
+    for (int s = 1; s < S; s++) acc = acc + p[s];
+#endif
+    return acc;
+}
+
+/*
+ * Non-finite inputs, decided per output from the whole rows x[m,:], w[n,:]
+ * (limitations page, corrections table; validation page claims table on IEEE
+ * specials): a NaN code anywhere in row m of x or row n of w makes the
+ * output the canonical NaN.
+ * Reading (E5M2 infinities; the pages record them but state no rule): a k
+ * with Inf times zero, or infinite products of both signs, give NaN;
+ * otherwise any infinite product gives that signed infinity.  This is the
+ * IEEE outcome of adding the products in any order, and it is the same
+ * whether taken over the whole row or per split / chunk and then added.
+ * Returns CLS_NAN, CLS_INF (with *neg) or CLS_FINITE.
+ */
+static int special_class(const operands *o, int64_t m, int64_t n, int *neg)
+{
+    int nan = 0, pos_inf = 0, neg_inf = 0;
+    for (int64_t k = 0; k < o->K; k++) {
+        fp8_val a = decode_fp8(x_at(o, m, k), o->xfmt);
+        fp8_val b = decode_fp8(w_at(o, n, k), o->wfmt);
+        if (a.cls == CLS_NAN || b.cls == CLS_NAN) { nan = 1; continue; }
+        if (a.cls == CLS_INF || b.cls == CLS_INF) {
+            if (a.cls == CLS_ZERO || b.cls == CLS_ZERO) { nan = 1; continue; }
+            if (a.s ^ b.s) neg_inf = 1; else pos_inf = 1;
+        }
+    }
+    if (nan || (pos_inf && neg_inf)) return CLS_NAN;
+    if (pos_inf || neg_inf) { *neg = neg_inf; return CLS_INF; }
+    return CLS_FINITE;
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE round-to-nearest-even of an exact value to a binary format with p
+ * significand bits and exponent range [emin, emax], subnormals kept
+ * (limitations page: flush-to-zero would change subnormal arithmetic and is
+ * refused).  The argument must be exact in double, which every caller
+ * guarantees (products of two binary32 values, binary32 values).
+ * Returns the rounded value (+-inf on overflow), with the sign of v. */
+static double round_to_format(double v, int p, int emin, int emax)
+{
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);
+    e -= 1;                       /* a in [2^e, 2^(e+1)) */
+    if (e < emin) e = emin;       /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, e - (p - 1));
+    double scaled = a / quantum;  /* exact: division by a power of two */
+    double fl = floor(scaled);
+    double rem = scaled - fl;     /* exact */
+    double r;
+    if (rem > 0.5) r = fl + 1.0;
+    else if (rem < 0.5) r = fl;
+    else r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    double res = r * quantum;
+    if (res >= ldexp(1.0, emax + 1)) res = INFINITY;
+    return v < 0 ? -res : res;
+}
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float f32_from(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+#if ORACLE_MUTANT == MUT_CANON_NAN
+#define CANON_NAN_F32 0x7FC00000u
+#define CANON_NAN_16 0x7FC0u
+#else
+/* Reading: the pages say NaN outputs are canonical without printing the bit
+ * pattern; 0x7FFFFFFF (binary32) and 0x7FFF (bf16, fp16) is the canonical
+ * NaN of NVIDIA's public PTX documentation.  Parity of this choice with
+ * hardware is unpinned. */
+#define CANON_NAN_F32 0x7FFFFFFFu
+#define CANON_NAN_16 0x7FFFu
+#endif
+
+/* binary32 product RN32(a*b) of two binary32 values (IEEE multiplication). */
+static float mul_f32(float a, float b)
+{
+    if (isnan(a) || isnan(b)) return NAN;
+    if ((isinf(a) && b == 0.0f) || (isinf(b) && a == 0.0f)) return NAN;
+    int neg = signbit(a) ^ signbit(b);
+    if (isinf(a) || isinf(b)) return neg ? -INFINITY : INFINITY;
+    double exact = (double)a * (double)b; /* 24x24 bits: exact in double */
+    if (exact == 0.0) return neg ? -0.0f : 0.0f;
+    return (float)round_to_format(exact, 24, -126, 127);
+}
+
+/*
+ * Epilogue, first rounding (limitations page, corrections table: the
+ * epilogue is y = fma(acc, alpha, +0) computed exactly; validation page,
+ * scope table row "Epilogue": alpha = fp32(scale_a * scale_b)):
+ * y32 = RN32(acc * alpha + (+0)).  An exactly zero product gives +0 (the
+ * sum -0 + +0 is +0 under round to nearest); a nonzero product that rounds
+ * to zero keeps its sign; overflow gives infinity.
+ */
+static float epilogue_f32(float acc, float alpha)
+{
+    if (isnan(acc) || isnan(alpha)) return NAN;
+    if ((isinf(acc) && alpha == 0.0f) || (isinf(alpha) && acc == 0.0f)) return NAN;
+    int neg = signbit(acc) ^ signbit(alpha);
+    if (isinf(acc) || isinf(alpha)) return neg ? -INFINITY : INFINITY;
+    double exact = (double)acc * (double)alpha;
+    if (exact == 0.0) {
+#if ORACLE_MUTANT == MUT_MUL_NOT_FMA
+        return neg ? -0.0f : 0.0f;
+#else
+        return 0.0f;
+#endif
+    }
+    return (float)round_to_format(exact, 24, -126, 127);
+}
+
+/* Second rounding: RNE of the binary32 value to the output format
+ * (validation page: bf16/fp16 outputs are rounded from the fp32 value,
+ * double rounding, shown on constructed ties). */
+static uint32_t encode_output(float y32, int out_dtype)
+{
+    if (out_dtype == OUT_FP32) {
+        if (isnan(y32)) return CANON_NAN_F32;
+        return f32_bits(y32);
+    }
+    if (isnan(y32)) return CANON_NAN_16;
+    if (out_dtype == OUT_BF16) {
+        double r = round_to_format((double)y32, 8, -126, 127);
+        /* r is exactly representable in bf16, hence in binary32; bf16 is the
+         * top half of the binary32 pattern */
+        return f32_bits((float)r) >> 16;
+    }
+    /* binary16 */
+    double r = round_to_format((double)y32, 11, -14, 15);
+    uint32_t sign = signbit(r) ? 0x8000u : 0u;
+    double a = fabs(r);
+    if (isinf(a)) return sign | 0x7C00u;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    e -= 1;
+    if (e < -14) return sign | (uint32_t)(a / ldexp(1.0, -24)); /* subnormal */
+    uint32_t frac = (uint32_t)(a / ldexp(1.0, e - 10)) - 1024u;
+    return sign | ((uint32_t)(e + 15) << 10) | frac;
+}
+
+#if ORACLE_MUTANT == MUT_SINGLE_ROUNDING
+static uint32_t encode_single_rounded(float acc, float alpha, int out_dtype)
+{
+    double exact = (double)acc * (double)alpha;
+    if (out_dtype == OUT_FP32 || isnan(exact) || isinf(exact) || exact == 0.0)
+        return encode_output(epilogue_f32(acc, alpha), out_dtype);
+    if (out_dtype == OUT_BF16)
+        return f32_bits((float)round_to_format(exact, 8, -126, 127)) >> 16;
+    return encode_output((float)round_to_format(exact, 11, -14, 15), out_dtype);
+}
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Exported entry points. */
+
+#define API __attribute__((visibility("default")))
+
+/* The accumulator before the epilogue for output (m, n): the per-split
+ * chains (fast) or chunked sums (slow), combined; non-finite inputs decided
+ * first.  Returns the binary32 bit pattern (NaN canonical). */
+static uint32_t acc_bits_at(const operands *o, int64_t m, int64_t n, int fast, int S,
+                            const oracle_profile *pf)
+{
+    int neg = 0;
+    int cls = special_class(o, m, n, &neg);
+    if (cls == CLS_NAN) return CANON_NAN_F32;
+    if (cls == CLS_INF) return neg ? 0xFF800000u : 0x7F800000u;
+    return f32_bits(finite_accumulator(o, m, n, fast, S, pf));
+}
+
+static uint32_t out_bits_from_acc(uint32_t acc_bits, float alpha, int out_dtype)
+{
+#if ORACLE_MUTANT == MUT_SINGLE_ROUNDING
+    return encode_single_rounded(f32_from(acc_bits), alpha, out_dtype);
+#else
+    return encode_output(epilogue_f32(f32_from(acc_bits), alpha), out_dtype);
+#endif
+}
+
+API int oracle_mutant_id(void) { return ORACLE_MUTANT; }
+
+API int oracle_decode(uint8_t code, int fmt, int *cls, int *s, int *e, int *M)
+{
+    fp8_val v = decode_fp8(code, fmt);
+    *cls = v.cls; *s = v.s; *e = v.e; *M = v.M;
+    return 0;
+}
+
+API uint32_t oracle_mul_f32(uint32_t a, uint32_t b) { return f32_bits(mul_f32(f32_from(a), f32_from(b))); }
+
+API uint32_t oracle_add_f32(uint32_t a, uint32_t b)
+{
+    float r = f32_from(a) + f32_from(b);
+    return isnan(r) ? CANON_NAN_F32 : f32_bits(r);
+}
+
+API uint32_t oracle_epilogue_f32(uint32_t acc, uint32_t alpha)
+{
+    float y = epilogue_f32(f32_from(acc), f32_from(alpha));
+    return isnan(y) ? CANON_NAN_F32 : f32_bits(y);
+}
+
+API uint32_t oracle_encode_output(uint32_t y32, int out_dtype) { return encode_output(f32_from(y32), out_dtype); }
+
+/* Full epilogue: alpha = RN32(sx*sw), then y = out(RN32(acc*alpha)). */
+API uint32_t oracle_output_from_acc(uint32_t acc_bits, uint32_t sx, uint32_t sw, int out_dtype)
+{
+    float alpha = mul_f32(f32_from(sx), f32_from(sw));
+    return out_bits_from_acc(acc_bits, alpha, out_dtype);
+}
+
+/* The exact chain of [k0, k1) for one output, starting from +0 (no specials,
+ * no split, no chunking).  Valid for any F up to 48. */
+API int oracle_chain_exact(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt,
+                           int64_t ldw, int64_t m, int64_t n, int64_t k0, int64_t k1, int B, int F,
+                           int *neg, int64_t *mag, int *q)
+{
+    if (B < 1 || B > MAX_B || F < 1 || F > 48) return -1;
+    operands o = {x, xfmt, ldx, w, wfmt, ldw, 0, 0, k1};
+    oracle_profile pf = {B, F, 128, 128};
+    exact_val r = chain_exact(&o, m, n, k0, k1, &pf, EXACT_PLUS_ZERO);
+    *neg = r.neg; *mag = r.mag; *q = r.q;
+    return 0;
+}
+
+/* One block step on explicit products: g[i], P[i], s[i] (P = 0 marks a zero
+ * product), incoming c = (-1)^c_neg * c_mag * 2^c_q. */
+API int oracle_block_step(const int *g, const int *P, const int *s, int n, int F, int c_neg,
+                          int64_t c_mag, int c_q, int *neg, int64_t *mag, int *q)
+{
+    if (n < 0 || n > MAX_B) return -1;
+    product buf[MAX_B];
+    for (int i = 0; i < n; i++) {
+        buf[i].cls = P[i] ? CLS_FINITE : CLS_ZERO;
+        buf[i].g = g[i]; buf[i].P = P[i]; buf[i].s = s[i];
+    }
+    exact_val c = {c_neg, c_mag, c_q};
+    exact_val r = block_step(c, buf, n, F);
+    *neg = r.neg; *mag = r.mag; *q = r.q;
+    return 0;
+}
+
+static int check_args(int B, int F, int S, int Q, int W, int xfmt, int wfmt)
+{
+    if (B < 1 || B > MAX_B || F < 1 || F > 23) return -1;
+    if (S < 1 || S > 4096 || Q < 1 || W < 1) return -1;
+    if ((xfmt != FMT_E4M3FN && xfmt != FMT_E5M2) || (wfmt != FMT_E4M3FN && wfmt != FMT_E5M2)) return -1;
+    return 0;
+}
+
+/* Accumulator and output at a list of (m, n) points. */
+API int oracle_points(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt, int64_t ldw,
+                      int64_t K, int64_t npts, const int64_t *ms, const int64_t *ns, uint32_t sx,
+                      uint32_t sw, int out_dtype, int fast, int S, int B, int F, int Q, int W,
+                      uint32_t *acc_out, uint32_t *y_out)
+{
+    if (check_args(B, F, S, Q, W, xfmt, wfmt)) return -1;
+    operands o = {x, xfmt, ldx, w, wfmt, ldw, 0, 0, K};
+    oracle_profile pf = {B, F, Q, W};
+    float alpha = mul_f32(f32_from(sx), f32_from(sw));
+    for (int64_t i = 0; i < npts; i++) {
+        uint32_t a = acc_bits_at(&o, ms[i], ns[i], fast, S, &pf);
+        if (acc_out) acc_out[i] = a;
+        if (y_out) y_out[i] = out_bits_from_acc(a, alpha, out_dtype);
+    }
+    return 0;
+}
+
+typedef struct {
+    const operands *o;
+    const oracle_profile *pf;
+    float alpha;
+    int out_dtype, fast, S;
+    uint32_t *acc_out, *y_out;
+    int64_t row_begin, row_end;
+} job;
+
+static void *run_rows(void *arg)
+{
+    job *j = (job *)arg;
+    for (int64_t m = j->row_begin; m < j->row_end; m++)
+        for (int64_t n = 0; n < j->o->N; n++) {
+            uint32_t a = acc_bits_at(j->o, m, n, j->fast, j->S, j->pf);
+            if (j->acc_out) j->acc_out[m * j->o->N + n] = a;
+            if (j->y_out) j->y_out[m * j->o->N + n] = out_bits_from_acc(a, j->alpha, j->out_dtype);
+        }
+    return NULL;
+}
+
+/* The whole [M, N] result, rows spread over nthreads host threads.
+ * acc_out and y_out are dense [M, N] arrays of bit patterns (either may be
+ * NULL).  y_out holds 16-bit patterns in the low half for bf16/fp16. */
+API int oracle_scaled_mm(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt,
+                         int64_t ldw, int64_t M, int64_t N, int64_t K, uint32_t sx, uint32_t sw,
+                         int out_dtype, int fast, int S, int B, int F, int Q, int W,
+                         uint32_t *acc_out, uint32_t *y_out, int nthreads)
+{
+    if (check_args(B, F, S, Q, W, xfmt, wfmt)) return -1;
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    operands o = {x, xfmt, ldx, w, wfmt, ldw, M, N, K};
+    oracle_profile pf = {B, F, Q, W};
+    float alpha = mul_f32(f32_from(sx), f32_from(sw));
+    pthread_t th[256];
+    job jobs[256];
+    int nt = (int)((M < nthreads) ? (M > 0 ? M : 1) : nthreads);
+    int64_t per = (M + nt - 1) / nt;
+    for (int t = 0; t < nt; t++) {
+        jobs[t].o = &o; jobs[t].pf = &pf; jobs[t].alpha = alpha;
+        jobs[t].out_dtype = out_dtype; jobs[t].fast = fast; jobs[t].S = S;
+        jobs[t].acc_out = acc_out; jobs[t].y_out = y_out;
+        jobs[t].row_begin = t * per < M ? t * per : M;
+        jobs[t].row_end = (t + 1) * per < M ? (t + 1) * per : M;
+    }
+    if (nt == 1) { run_rows(&jobs[0]); return 0; }
+    for (int t = 0; t < nt; t++) pthread_create(&th[t], NULL, run_rows, &jobs[t]);
+    for (int t = 0; t < nt; t++) pthread_join(th[t], NULL);
+    return 0;
+}
