@@ -1,0 +1,198 @@
+"""Benchmark of the bit-exact emulated FP8 GEMM on one MI355X.
+
+One step is one emulated scaled GEMM over the whole workload (decode, block
+chains, epilogue; and the split combination when the workload splits), with
+the FP8 operands, scales, output and workspace already resident in HBM.
+Prints one JSON line.
+
+Metric: emulated GEMM-ops/s = 2*M*N*K / t, and the fraction of the
+integer-VALU roofline R.  R counts 7 integer operations per multiply-add
+(exponent add, block maximum, alignment distance, significand product,
+shift-truncate, sign, accumulate) at the packed 16-bit VALU rate:
+256 CUs x 64 lanes x 2.4 GHz x 2 ops / 7 = 22.47e12 GEMM-ops/s.
+
+cpu_baseline: the CPU oracle, untuned, timed on the host on a bounded sample
+of the same workload (whole rows of the output), and checked bit for bit
+against the GPU's output on that sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from bit_exact_fp8_amd import api  # noqa: E402
+from bit_exact_fp8_amd.inputs import (FP8_DTYPES, OUT_DTYPES, WORKLOADS, make_operands,  # noqa: E402
+                                      scale_bits)
+
+PEAK_ALU = 256 * 64 * 2.4e9 * 2 / 7 * 2  # GEMM-ops/s: (packed int ops/s) / (7 ops per MAC) * (2 ops per MAC)
+METRIC = "bit-exact emulated FP8 GEMM ops/s (2MNK/s) and % of int-VALU roofline"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    one exists for this workload and the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"traffic_main_kernel_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        src = os.path.join(ROOT, "bit_exact_fp8_amd", "csrc", "emu_kernels.hip")
+        import hashlib
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if d.get("kernel_source_sha256") != digest:
+            return None
+        return d.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x, w, y_gpu, budget_s: float):
+    """Time the oracle on whole output rows, sized to about budget_s seconds."""
+    import oracle
+    orc = oracle.default()
+    threads = min(16, os.cpu_count() or 1)
+    xs, ws = x.numpy(), w.numpy()
+    sx, sw = scale_bits(wl.scale_x), scale_bits(wl.scale_w)
+    # probe the rate on a small sample
+    rows_probe = min(wl.M, threads)
+    cols_probe = min(wl.N, 256)
+    t0 = time.perf_counter()
+    orc.scaled_mm(xs[:rows_probe], wl.xfmt, ws[:cols_probe], wl.wfmt, sx, sw, wl.out, wl.fast, wl.split_S,
+                  threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    rate = rows_probe * cols_probe * wl.K / dt  # MAC/s
+    rows = int(max(threads, min(wl.M, budget_s * rate / (wl.N * wl.K))))
+    rows = max(threads, (rows // threads) * threads)
+    rows = min(rows, wl.M)
+    t0 = time.perf_counter()
+    acc, y = orc.scaled_mm(xs[:rows], wl.xfmt, ws, wl.wfmt, sx, sw, wl.out, wl.fast, wl.split_S,
+                           threads=threads)
+    dt = time.perf_counter() - t0
+    ops = 2 * rows * wl.N * wl.K
+    same = bool(np.array_equal(y, y_gpu[:rows]))
+    return {"value": ops / dt, "unit": "GEMM-ops/s", "cores": threads, "kind": "oracle",
+            "sample": f"output rows 0..{rows - 1} (all {wl.N} columns, K={wl.K}) of the workload, "
+                      f"{ops / 2:.3g} MACs in {dt:.1f} s",
+            "gpu_bit_exact_on_sample": same}
+
+
+def output_bits(t):
+    t = t.cpu()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed_8192", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(one process, one MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {wl.name} inputs (seed {args.seed})")
+    x, w = make_operands(wl, args.seed)
+    xd = x.to(dev).view(FP8_DTYPES[wl.xfmt])
+    wd = w.to(dev).view(FP8_DTYPES[wl.wfmt])
+    sxd = torch.tensor([wl.scale_x], dtype=torch.float32, device=dev)
+    swd = torch.tensor([wl.scale_w], dtype=torch.float32, device=dev)
+    out = torch.empty((wl.M, wl.N), dtype=OUT_DTYPES[wl.out], device=dev)
+    ws_bytes = api.workspace_bytes(wl.M, wl.N, wl.K, wl.split_S, wl.fast)
+    wsbuf = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    lib = api._lib()
+    stream = torch.cuda.current_stream(dev)
+    call_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
+                 wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), out.data_ptr(), api.OUT_DTYPE[out.dtype],
+                 wl.N, int(wl.fast), wl.split_S, 0, wsbuf.data_ptr(), ws_bytes, stream.cuda_stream)
+
+    def step():
+        st = lib.emu_scaled_mm(*call_args)
+        if st != 0:
+            raise api.EmuError(st, lib.emu_last_error_message().decode())
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    log(f"[bench] timing {args.steps} steps")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    launch_ms = float(np.mean(ev_ms))
+    ops = wl.gemm_ops
+    value = ops * args.steps / wall
+    achieved = ops / (launch_ms * 1e-3)
+
+    traffic = load_traffic(wl.name)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GEMM-ops/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {**wl.describe(), "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved / 1e12,
+            "peak": PEAK_ALU / 1e12,
+            "unit": "T GEMM-ops/s",
+            "frac": achieved / PEAK_ALU,
+            "traffic": traffic,
+            "launch_ms": launch_ms,
+            "launch_ms_min": float(np.min(ev_ms)),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: timing the oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, x, w, output_bits(out), args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""Thin ctypes binding of ``libemu_fp8gemm.so`` (C ABI in ``include/emu_fp8gemm.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library's kernels.  PyTorch supplies device memory and the current stream.
+There is no CPU fallback: without the built library every call raises.
+
+``scaled_mm`` keeps the argument order of ``torch._scaled_mm`` as the mmaemu
+user guide (section 3) describes it: ``mat1`` is ``[M, K]`` row-major, ``mat2``
+is ``[K, N]`` column-major, i.e. ``w.t()`` for a row-major weight ``w [N, K]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libemu_fp8gemm.so"
+
+# Enumerations of include/emu_fp8gemm.h
+EMU_OK, EMU_ERR_INVALID_ARG, EMU_ERR_REJECTED, EMU_ERR_UNSUPPORTED, EMU_ERR_WORKSPACE, EMU_ERR_DEVICE = range(6)
+FP8_FORMAT = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
+FP8_FORMAT_NAME = {"e4m3fn": 0, "e5m2": 1}
+OUT_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+PROFILE = {"hopper": 0}
+
+
+class EmuError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"emu status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIBNAME)
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run __graft_entry__.build() (there is no CPU fallback)")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    common = [vp, i32, i64, vp, i32, i64, i64, i64, i64]
+    lib.emu_scaled_mm.argtypes = common + [vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.emu_scaled_mm.restype = i32
+    lib.emu_accumulate.argtypes = common + [vp, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.emu_accumulate.restype = i32
+    lib.emu_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.emu_workspace_bytes.restype = ctypes.c_size_t
+    lib.emu_status_string.argtypes = [i32]
+    lib.emu_status_string.restype = ctypes.c_char_p
+    lib.emu_last_error_message.restype = ctypes.c_char_p
+    lib.emu_abi_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def abi_version() -> int:
+    return _lib().emu_abi_version()
+
+
+def _check(status: int):
+    if status != EMU_OK:
+        lib = _lib()
+        raise EmuError(status, (lib.emu_last_error_message() or b"").decode())
+
+
+def workspace_bytes(M: int, N: int, K: int, split_S: int = 1, use_fast_accum: bool = True,
+                    profile: str = "hopper") -> int:
+    return int(_lib().emu_workspace_bytes(M, N, K, split_S, int(use_fast_accum), PROFILE[profile]))
+
+
+def _fmt(t: torch.Tensor) -> int:
+    if t.dtype in FP8_FORMAT:
+        return FP8_FORMAT[t.dtype]
+    raise TypeError(f"expected a float8_e4m3fn or float8_e5m2 tensor, got {t.dtype}")
+
+
+def _scale_ptr(s: torch.Tensor, device) -> int:
+    if not isinstance(s, torch.Tensor) or s.numel() != 1 or s.dtype != torch.float32:
+        raise ValueError("tensor-wise scales must be one-element float32 tensors")
+    if s.device != device:
+        raise ValueError("scales must live on the operands' device")
+    return s.data_ptr()
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _operands(mat1, mat2):
+    if mat1.dim() != 2 or mat2.dim() != 2:
+        raise ValueError("mat1 and mat2 must be 2-D")
+    M, K = mat1.shape
+    K2, N = mat2.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if mat1.stride(1) != 1 and M > 1:
+        raise ValueError("mat1 must be row-major [M, K]")
+    w = mat2.t()  # [N, K]
+    if w.stride(1) != 1 and N > 1:
+        raise ValueError("mat2 must be column-major [K, N] (pass w.t() for a row-major w)")
+    ldx = mat1.stride(0) if (M > 1 and K > 0) else K
+    ldw = w.stride(0) if (N > 1 and K > 0) else K
+    return mat1, w, M, N, K, ldx, ldw
+
+
+def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
+              out_dtype=None, use_fast_accum: bool = False, split_S: int = 1,
+              profile: str = "hopper", out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = (mat1 @ mat2) * scale_a * scale_b with the emulated FP8 arithmetic.
+
+    Defaults follow torch (user guide, section 3): use_fast_accum=False and
+    out_dtype = the input dtype (FP8 outputs are not built and raise)."""
+    x, w, M, N, K, ldx, ldw = _operands(mat1, mat2)
+    if out_dtype is None:
+        out_dtype = mat1.dtype
+    if out_dtype not in OUT_DTYPE:
+        raise EmuError(EMU_ERR_UNSUPPORTED, f"output dtype {out_dtype} is not supported")
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    elif out.shape != (M, N) or out.dtype != out_dtype or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a row-major [M, N] tensor of out_dtype")
+    ldo = out.stride(0) if M > 1 else N
+    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
+    wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    lib = _lib()
+    _check(lib.emu_scaled_mm(x.data_ptr(), _fmt(x), ldx, w.data_ptr(), _fmt(w), ldw, M, N, K,
+                             _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), out.data_ptr(),
+                             OUT_DTYPE[out_dtype], ldo, int(use_fast_accum), int(split_S),
+                             PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev)))
+    return out
+
+
+def accumulate(x: torch.Tensor, w: torch.Tensor, use_fast_accum: bool, split_S: int = 1,
+               profile: str = "hopper") -> torch.Tensor:
+    """The fp32 accumulator before the epilogue.  Both operands are [rows, K]
+    (user guide, section 3: accumulate takes w, not w.t(), and has no default
+    for use_fast_accum)."""
+    xx, ww, M, N, K, ldx, ldw = _operands(x, w.t())
+    dev = xx.device
+    acc = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ldacc = acc.stride(0) if M > 1 else N
+    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
+    wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    lib = _lib()
+    _check(lib.emu_accumulate(xx.data_ptr(), _fmt(xx), ldx, ww.data_ptr(), _fmt(ww), ldw, M, N, K,
+                              acc.data_ptr(), ldacc, int(use_fast_accum), int(split_S),
+                              PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev)))
+    return acc

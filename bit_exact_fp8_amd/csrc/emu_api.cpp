@@ -1,0 +1,237 @@
+// emu_api.cpp -- the C ABI of include/emu_fp8gemm.h: argument checks, launch
+// planning and kernel launches on the caller's stream.  No device memory is
+// allocated here and the stream is never synchronised.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string>
+
+#include "../../include/emu_fp8gemm.h"
+#include "emu_internal.h"
+#include "fp_round.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+emu_status fail(emu_status s, const std::string &msg)
+{
+    g_last_error = msg;
+    return s;
+}
+
+emu_status ok()
+{
+    g_last_error.clear();
+    return EMU_OK;
+}
+
+constexpr int64_t kSplitTile = 128;  // hopper profile: 128-wide k-tiles
+constexpr int kMaxSplits = 65535;    // one grid dimension
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+    int S;
+    int64_t split_len;
+};
+
+Plan make_plan(int64_t K, int S)
+{
+    // nt = ceil(K/128) k-tiles, tps = ceil(nt/S) per split; split s covers
+    // [s*tps*128, min((s+1)*tps*128, K)) (validation page, scope table row
+    // "Split-K on the H100 PCIe": contiguous runs of 128-wide k-tiles).
+    Plan p;
+    p.S = S;
+    const int64_t nt = (K + kSplitTile - 1) / kSplitTile;
+    const int64_t tps = (nt + S - 1) / S;
+    p.split_len = (S == 1) ? (K > 0 ? K : 1) : (tps > 0 ? tps * kSplitTile : kSplitTile);
+    if (S == 1 && p.split_len % kSplitTile) p.split_len += kSplitTile - p.split_len % kSplitTile;
+    return p;
+}
+
+// Pick the largest workgroup tile that still gives the GPU enough workgroups.
+int choose_tile(int64_t M, int64_t N, int S)
+{
+    const int order[] = {emu::TILE_64x128, emu::TILE_32x64, emu::TILE_16x16};
+    for (int cfg : order) {
+        const emu::TileShape t = emu::tile_shape(cfg);
+        const int64_t wgs = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * S;
+        if (wgs >= 512) return cfg;
+    }
+    return emu::TILE_16x16;
+}
+
+emu_status check_common(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w,
+                        emu_fp8_format wf, int64_t ldw, int64_t M, int64_t N, int64_t K, int split_S,
+                        emu_profile profile)
+{
+    if (M < 0 || N < 0 || K < 0) return fail(EMU_ERR_INVALID_ARG, "negative dimension");
+    if ((xf != EMU_FP8_E4M3FN && xf != EMU_FP8_E5M2) || (wf != EMU_FP8_E4M3FN && wf != EMU_FP8_E5M2))
+        return fail(EMU_ERR_INVALID_ARG, "unknown FP8 format");
+    if (split_S < 1) return fail(EMU_ERR_INVALID_ARG, "split_S must be >= 1");
+    if (profile != EMU_PROFILE_HOPPER) return fail(EMU_ERR_UNSUPPORTED, "only the hopper profile is built");
+    if (split_S > kMaxSplits) return fail(EMU_ERR_UNSUPPORTED, "split_S above 65535");
+    if (ldx < K || ldw < K) return fail(EMU_ERR_INVALID_ARG, "leading dimension smaller than K");
+    if (xf == EMU_FP8_E5M2 && wf == EMU_FP8_E5M2)
+        return fail(EMU_ERR_REJECTED, "e5m2 x e5m2 is rejected (as torch does)");
+    if (K % 16 || N % 16) return fail(EMU_ERR_REJECTED, "K and N must be multiples of 16");
+    if (ldx % 16 || ldw % 16) return fail(EMU_ERR_REJECTED, "ldx and ldw must be multiples of 16");
+    if (M > 0 && N > 0 && K > 0) {
+        if (!x || !w) return fail(EMU_ERR_INVALID_ARG, "null operand pointer");
+        if (!aligned16(x) || !aligned16(w)) return fail(EMU_ERR_REJECTED, "operands must be 16-byte aligned");
+    }
+    if (M > INT32_MAX || N > INT32_MAX) return fail(EMU_ERR_UNSUPPORTED, "M or N above 2^31-1");
+    return EMU_OK;
+}
+
+emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w, emu_fp8_format wf,
+               int64_t ldw, int64_t M, int64_t N, int64_t K, const float *sx, const float *sw, void *out,
+               int out_kind, size_t out_elem, int64_t ldo, int fast, int S, void *workspace,
+               size_t workspace_bytes, void *stream_ptr)
+{
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    const Plan plan = make_plan(K, S);
+    const int cfg = choose_tile(M, N, S);
+    const emu::TileShape ts = emu::tile_shape(cfg);
+    const int64_t rows_per_launch = kMaxGridY * ts.bm;
+
+    emu::MainParams p{};
+    p.ldx = ldx;
+    p.ldw = ldw;
+    p.N = (int)N;
+    p.K = K;
+    p.split_len = plan.split_len;
+    p.fast = fast ? 1 : 0;
+    p.scale_x = sx;
+    p.scale_w = sw;
+    p.w = w;
+    if (S == 1) {
+        p.out_kind = out_kind;
+        p.ldo = ldo;
+        p.split_stride = 0;
+    } else {
+        p.out_kind = emu::OUT_ACC_F32;
+        p.ldo = N;
+        p.split_stride = M * N;
+    }
+    for (int64_t m_start = 0; m_start < M; m_start += rows_per_launch) {
+        const int64_t rows = (M - m_start < rows_per_launch) ? M - m_start : rows_per_launch;
+        p.x = x ? x + m_start * ldx : nullptr;
+        p.M = (int)rows;
+        if (S == 1)
+            p.out = static_cast<char *>(out) + m_start * ldo * (int64_t)out_elem;
+        else
+            p.out = static_cast<char *>(workspace) + m_start * N * 4;
+        hipError_t e = emu::launch_main(cfg, xf, wf, p, S, stream);
+        if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("main kernel launch: ") + hipGetErrorString(e));
+    }
+    if (S > 1) {
+        emu::CombineParams c{};
+        c.part = static_cast<const float *>(workspace);
+        c.S = S;
+        c.M = (int)M;
+        c.N = (int)N;
+        c.out_kind = out_kind;
+        c.out = out;
+        c.ldo = ldo;
+        c.scale_x = sx;
+        c.scale_w = sw;
+        hipError_t e = emu::launch_combine(c, stream);
+        if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    }
+    (void)workspace_bytes;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum, emu_profile profile)
+{
+    (void)K;
+    (void)fast_accum;
+    (void)profile;
+    if (M < 0 || N < 0 || split_S < 1) return 0;
+    if (split_S == 1) return 0;
+    return (size_t)split_S * (size_t)M * (size_t)N * sizeof(float);
+}
+
+emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
+                         emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                         const float *scale_x, const float *scale_w, void *out, emu_out_dtype out_dtype,
+                         int64_t ldo, int fast_accum, int split_S, emu_profile profile, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    emu_status s = check_common(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, split_S, profile);
+    if (s != EMU_OK) return s;
+    int kind;
+    size_t elem;
+    switch (out_dtype) {
+    case EMU_OUT_BF16: kind = emu::OUT_BF16; elem = 2; break;
+    case EMU_OUT_FP16: kind = emu::OUT_F16; elem = 2; break;
+    case EMU_OUT_FP32: kind = emu::OUT_F32; elem = 4; break;
+    default:
+        if ((int)out_dtype >= 3 && (int)out_dtype <= 4)
+            return fail(EMU_ERR_UNSUPPORTED, "FP8 outputs are not built");
+        return fail(EMU_ERR_INVALID_ARG, "unknown output dtype");
+    }
+    if (ldo < N) return fail(EMU_ERR_INVALID_ARG, "ldo smaller than N");
+    if (M == 0 || N == 0) return ok();
+    if (!out || !scale_x || !scale_w) return fail(EMU_ERR_INVALID_ARG, "null output or scale pointer");
+    if (!aligned16(out)) return fail(EMU_ERR_REJECTED, "out must be 16-byte aligned");
+    const size_t need = emu_workspace_bytes(M, N, K, split_S, fast_accum, profile);
+    if (workspace_bytes < need || (need && !workspace))
+        return fail(EMU_ERR_WORKSPACE, "workspace smaller than emu_workspace_bytes()");
+    if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, scale_x, scale_w, out, kind, elem, ldo, fast_accum,
+               split_S, workspace, workspace_bytes, stream);
+}
+
+emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
+                          emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K, float *acc,
+                          int64_t ldacc, int fast_accum, int split_S, emu_profile profile, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    emu_status s = check_common(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, split_S, profile);
+    if (s != EMU_OK) return s;
+    if (ldacc < N) return fail(EMU_ERR_INVALID_ARG, "ldacc smaller than N");
+    if (M == 0 || N == 0) return ok();
+    if (!acc) return fail(EMU_ERR_INVALID_ARG, "null accumulator pointer");
+    if (reinterpret_cast<uintptr_t>(acc) & 3u) return fail(EMU_ERR_INVALID_ARG, "acc must be 4-byte aligned");
+    const size_t need = emu_workspace_bytes(M, N, K, split_S, fast_accum, profile);
+    if (workspace_bytes < need || (need && !workspace))
+        return fail(EMU_ERR_WORKSPACE, "workspace smaller than emu_workspace_bytes()");
+    if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    // The scale pointers are not read for the accumulator.
+    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, nullptr, nullptr, acc, emu::OUT_ACC_F32, 4, ldacc,
+               fast_accum, split_S, workspace, workspace_bytes, stream);
+}
+
+const char *emu_status_string(emu_status status)
+{
+    switch (status) {
+    case EMU_OK: return "ok";
+    case EMU_ERR_INVALID_ARG: return "invalid argument";
+    case EMU_ERR_REJECTED: return "rejected (a call torch / cuBLASLt would refuse)";
+    case EMU_ERR_UNSUPPORTED: return "unsupported feature";
+    case EMU_ERR_WORKSPACE: return "workspace too small";
+    case EMU_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char *emu_last_error_message(void) { return g_last_error.c_str(); }
+
+int emu_abi_version(void) { return EMU_ABI_VERSION; }
+
+uint32_t emu_host_mul_f32(uint32_t a, uint32_t b) { return emu::mul_f32(a, b); }
+uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha) { return emu::canon_f32(emu::epilogue_f32(acc, alpha)); }
+uint16_t emu_host_f32_to_bf16(uint32_t f) { return emu::f32_to_bf16(f); }
+uint16_t emu_host_f32_to_f16(uint32_t f) { return emu::f32_to_f16(f); }
+
+}  // extern "C"

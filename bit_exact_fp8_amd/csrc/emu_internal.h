@@ -1,0 +1,54 @@
+// emu_internal.h -- launch plan shared by the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace emu {
+
+// What the main kernel writes for each output.
+enum OutKind : int {
+    OUT_ACC_F32 = 0,  // binary32 accumulator (NaN canonical); also split partials
+    OUT_BF16 = 1,     // epilogue, bf16
+    OUT_F16 = 2,      // epilogue, binary16
+    OUT_F32 = 3,      // epilogue, binary32
+};
+
+struct MainParams {
+    const uint8_t *x;      // [M, K] codes, row stride ldx bytes
+    const uint8_t *w;      // [N, K] codes, row stride ldw bytes
+    int64_t ldx, ldw;
+    int M, N;              // rows of this launch (M may be a slice)
+    int64_t K;
+    int64_t split_len;     // K-length of every split, a multiple of 128 (>= K when unsplit)
+    int fast;              // 1: one chain per split; 0: restart every 128
+    int out_kind;          // OutKind
+    void *out;             // OUT_ACC_F32 / epilogue destination, [M, N] with row stride ldo elements
+    int64_t ldo;
+    int64_t split_stride;  // elements between consecutive splits' partials in `out` (S > 1)
+    const float *scale_x, *scale_w;
+};
+
+struct CombineParams {
+    const float *part;     // [S, M, N] partials, dense
+    int S, M, N;
+    int out_kind;          // OUT_ACC_F32 or an epilogue kind
+    void *out;
+    int64_t ldo;
+    const float *scale_x, *scale_w;
+};
+
+// Tile configurations of the main kernel (rows x cols per workgroup, and
+// per thread).
+enum TileConfig : int { TILE_64x128 = 0, TILE_32x64 = 1, TILE_16x16 = 2, TILE_COUNT = 3 };
+
+struct TileShape {
+    int bm, bn, threads;
+};
+TileShape tile_shape(int cfg);
+
+// Enqueue one main-kernel launch over grid (ceil(N/bn), ceil(M/bm), S).
+hipError_t launch_main(int cfg, int xfmt, int wfmt, const MainParams &p, int S, hipStream_t stream);
+hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+
+}  // namespace emu

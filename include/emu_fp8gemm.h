@@ -1,0 +1,156 @@
+/*
+ * emu_fp8gemm.h -- C ABI of the MI355X (gfx950) bit-exact emulated FP8 GEMM.
+ *
+ * Computes y = (x @ w.T) * scale_x * scale_w with the arithmetic that the
+ * mmaemu v0.1 documentation describes for its default "hopper" profile
+ * (user guide section 1 and section 3 "A first GEMM"; validation page,
+ * scope table rows "Hopper preset", "Slow accumulation", "Split-K on the
+ * H100 PCIe" and "Epilogue"; limitations page, corrections table):
+ *
+ *  - E4M3/E5M2 products are added in blocks of 32 consecutive products; each
+ *    block, together with the incoming accumulator, is aligned to the block's
+ *    largest exponent (field exponents, subnormals at emin), every term is cut
+ *    toward zero to 13 fraction bits, and the block sum is cut toward zero to
+ *    14 significant bits; a zero block result is +0.
+ *  - fast_accum != 0 chains the blocks along K; fast_accum == 0 restarts the
+ *    chain every 128 K and adds the chunk results in K order in binary32
+ *    round-to-nearest-even.
+ *  - split_S > 1 splits K into contiguous runs of 128-wide k-tiles,
+ *    ceil(ceil(K/128)/S) tiles per split (trailing splits may be empty and
+ *    give +0), and adds the partials serially, p0 + p1 + ... in binary32.
+ *  - the epilogue is alpha = RN32(scale_x * scale_w), y32 = RN32(acc*alpha+(+0))
+ *    (an exactly zero product gives +0), then round-to-nearest-even to the
+ *    output type; subnormals are kept everywhere.
+ *  - a NaN code anywhere in row m of x or row n of w makes output (m, n) the
+ *    canonical NaN (0x7FFFFFFF for fp32, 0x7FFF for bf16/fp16).  E5M2
+ *    infinities follow IEEE: Inf*0 or infinite products of both signs give
+ *    NaN, otherwise the signed infinity.
+ *
+ * Layouts (all pointers are device pointers owned by the caller):
+ *   x   [M, K] row-major FP8 codes, leading dimension ldx (bytes >= K);
+ *   w   [N, K] row-major FP8 codes, leading dimension ldw (this is torch's
+ *       mat2 = w.t(), a [K, N] column-major matrix);
+ *   out [M, N] row-major, leading dimension ldo (elements >= N);
+ *   scale_x, scale_w: one binary32 value each, read on the device.
+ *
+ * Ordering and ownership: every call only enqueues kernels on `stream` and
+ * returns; it never synchronises and never allocates device memory.  The
+ * caller keeps all buffers alive until the stream has run the work.  `out`
+ * is fully overwritten and never read.  Results are deterministic: no
+ * atomics take part in the arithmetic.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a
+ * non-OK status means nothing was written.  emu_last_error_message() gives
+ * a thread-local explanation of the last non-OK status.
+ */
+#ifndef EMU_FP8GEMM_H
+#define EMU_FP8GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EMU_ABI_VERSION 1
+
+#if defined(EMU_BUILDING_LIBRARY)
+#define EMU_API __attribute__((visibility("default")))
+#else
+#define EMU_API
+#endif
+
+typedef enum {
+    EMU_OK = 0,
+    EMU_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad leading dimension, unknown enum, split_S < 1 */
+    EMU_ERR_REJECTED = 2,    /* a call torch 2.7.1 / cuBLASLt would reject (limitations page, features table):
+                                e5m2 x e5m2, K or N not a multiple of 16, x / w / out not 16-byte aligned,
+                                ldx or ldw not a multiple of 16 */
+    EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: FP8 outputs, profiles other than hopper */
+    EMU_ERR_WORKSPACE = 4,   /* workspace_bytes < emu_workspace_bytes(...) */
+    EMU_ERR_DEVICE = 5       /* a HIP launch or runtime error */
+} emu_status;
+
+typedef enum { EMU_FP8_E4M3FN = 0, EMU_FP8_E5M2 = 1 } emu_fp8_format;
+
+/* 3 and 4 are reserved for FP8 outputs (e4m3fn, e5m2), which this library
+ * does not build: they return EMU_ERR_UNSUPPORTED. */
+typedef enum {
+    EMU_OUT_BF16 = 0,
+    EMU_OUT_FP16 = 1,
+    EMU_OUT_FP32 = 2,
+    EMU_OUT_E4M3FN = 3,
+    EMU_OUT_E5M2 = 4
+} emu_out_dtype;
+
+/* The arithmetic profile.  Only the default H100 PCIe profile "hopper" is
+ * built (user guide section 4: hopper is the default). */
+typedef enum { EMU_PROFILE_HOPPER = 0 } emu_profile;
+
+/*
+ * y = (x @ w.T) * scale_x * scale_w (torch._scaled_mm semantics with
+ * tensor-wise scales; user guide section 3).
+ *
+ * M >= 0 (any value), N >= 0 and K >= 0 multiples of 16.  M = 0 or N = 0
+ * returns EMU_OK without enqueuing anything; K = 0 writes +0 everywhere.
+ * workspace: device memory of at least emu_workspace_bytes(M, N, K, split_S,
+ * fast_accum, profile) bytes (may be NULL when that is 0); its contents on
+ * entry do not matter.  stream: a hipStream_t (NULL = the default stream).
+ */
+EMU_API emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
+                         const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
+                         int64_t M, int64_t N, int64_t K,
+                         const float *scale_x, const float *scale_w,
+                         void *out, emu_out_dtype out_dtype, int64_t ldo,
+                         int fast_accum, int split_S, emu_profile profile,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The binary32 accumulator before the epilogue: acc [M, N] row-major with
+ * leading dimension ldacc (mmaemu's accumulate(x, w, use_fast_accum), user
+ * guide section 3).  NaN results are 0x7FFFFFFF.  Same rules for the
+ * operands, workspace and stream as emu_scaled_mm.
+ */
+EMU_API emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
+                          const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
+                          int64_t M, int64_t N, int64_t K,
+                          float *acc, int64_t ldacc,
+                          int fast_accum, int split_S, emu_profile profile,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device workspace the two calls above need: split_S * M * N * 4 bytes when
+ * split_S > 1, otherwise 0.  Returns 0 for invalid sizes. */
+EMU_API size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum,
+                           emu_profile profile);
+
+/* Static description of a status code. */
+EMU_API const char *emu_status_string(emu_status status);
+
+/* Thread-local detail text of the last non-OK status returned on this thread
+ * (empty string if none).  The pointer stays valid until the next call on
+ * the same thread. */
+EMU_API const char *emu_last_error_message(void);
+
+/* EMU_ABI_VERSION of the built library. */
+EMU_API int emu_abi_version(void);
+
+/*
+ * Host builds of the library's own IEEE rounding routines, the same source
+ * its kernels use, exported so that CPU tests can check them without a GPU.
+ * All arguments and results are bit patterns.
+ *   emu_host_mul_f32:      RN32(a * b), IEEE binary32 multiplication.
+ *   emu_host_epilogue_f32: RN32(acc * alpha + (+0)); NaN results 0x7FFFFFFF.
+ *   emu_host_f32_to_bf16 / emu_host_f32_to_f16: round to nearest even,
+ *       subnormals kept, overflow to infinity, NaN -> 0x7FFF.
+ */
+EMU_API uint32_t emu_host_mul_f32(uint32_t a, uint32_t b);
+EMU_API uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha);
+EMU_API uint16_t emu_host_f32_to_bf16(uint32_t f);
+EMU_API uint16_t emu_host_f32_to_f16(uint32_t f);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMU_FP8GEMM_H */

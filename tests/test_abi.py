@@ -1,0 +1,176 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/*.h declares, rejects bad arguments on the host before touching the
+device, and its host-built IEEE rounding routines match numpy / torch."""
+import ctypes
+import glob
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from bit_exact_fp8_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(emu_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(api.library_path()), "build the library first (__graft_entry__.build())"
+    return api._lib()
+
+
+def test_headers_exist():
+    assert HEADERS
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert "emu_scaled_mm" in names and "emu_accumulate" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared but not exported"
+
+
+def test_abi_version(lib):
+    assert api.abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.emu_status_string(s)
+
+
+def test_workspace_bytes():
+    assert api.workspace_bytes(16, 256, 65536, 8) == 8 * 16 * 256 * 4
+    assert api.workspace_bytes(64, 5760, 1920, 1) == 0
+    assert api._lib().emu_workspace_bytes(-1, 16, 16, 2, 1, 0) == 0
+
+
+def call(lib, x=16, xf=0, ldx=32, w=16, wf=0, ldw=32, M=4, N=16, K=32, sx=4, sw=4, out=16,
+         od=0, ldo=16, fast=1, S=1, prof=0, ws=0, wsb=0):
+    """emu_scaled_mm with fake (never dereferenced) device addresses: every
+    case here must fail its host-side checks before any launch."""
+    return lib.emu_scaled_mm(x, xf, ldx, w, wf, ldw, M, N, K, sx, sw, out, od, ldo, fast, S, prof, ws,
+                             wsb, None)
+
+
+CASES = [
+    (dict(M=-1), api.EMU_ERR_INVALID_ARG),
+    (dict(K=-16), api.EMU_ERR_INVALID_ARG),
+    (dict(xf=7), api.EMU_ERR_INVALID_ARG),
+    (dict(S=0), api.EMU_ERR_INVALID_ARG),
+    (dict(ldx=16), api.EMU_ERR_INVALID_ARG),
+    (dict(ldo=8), api.EMU_ERR_INVALID_ARG),
+    (dict(od=9), api.EMU_ERR_INVALID_ARG),
+    (dict(x=0), api.EMU_ERR_INVALID_ARG),
+    (dict(sx=0), api.EMU_ERR_INVALID_ARG),
+    (dict(out=0), api.EMU_ERR_INVALID_ARG),
+    (dict(xf=1, wf=1), api.EMU_ERR_REJECTED),   # e5m2 x e5m2
+    (dict(K=24, ldx=32, ldw=32), api.EMU_ERR_REJECTED),
+    (dict(N=24, ldo=24), api.EMU_ERR_REJECTED),
+    (dict(x=24), api.EMU_ERR_REJECTED),          # misaligned storage
+    (dict(out=24), api.EMU_ERR_REJECTED),
+    (dict(ldx=40), api.EMU_ERR_REJECTED),
+    (dict(od=3), api.EMU_ERR_UNSUPPORTED),       # FP8 outputs
+    (dict(od=4), api.EMU_ERR_UNSUPPORTED),
+    (dict(prof=1), api.EMU_ERR_UNSUPPORTED),
+    (dict(S=2), api.EMU_ERR_WORKSPACE),
+    (dict(S=2, ws=16, wsb=100), api.EMU_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,status", CASES)
+def test_host_side_rejections(lib, kw, status):
+    assert call(lib, **kw) == status
+    assert lib.emu_last_error_message()
+
+
+def test_empty_problem_is_ok_without_launch(lib):
+    assert call(lib, M=0) == api.EMU_OK
+    assert call(lib, N=0, ldo=0) == api.EMU_OK
+
+
+def test_accumulate_rejections(lib):
+    f = lib.emu_accumulate
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 0, 16, 1, 1, 0, 0, 0, None) == api.EMU_ERR_INVALID_ARG
+    assert f(16, 1, 32, 16, 1, 32, 4, 16, 32, 16, 16, 1, 1, 0, 0, 0, None) == api.EMU_ERR_REJECTED
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 16, 16, 1, 3, 0, 16, 3 * 4 * 16 * 4 - 1, None) == api.EMU_ERR_WORKSPACE
+
+
+def test_page_parameters_match_the_library_split_rule():
+    """The split layout the library documents is the pages' contiguous rule
+    with 128-wide k-tiles (golden page_parameters.json)."""
+    params = json.load(open(os.path.join(ROOT, "tests", "golden", "page_parameters.json")))["hopper"]
+    hdr = open(os.path.join(ROOT, "include", "emu_fp8gemm.h")).read()
+    assert params["split_tile"]["value"] == 128 and "128-wide k-tiles" in hdr
+    assert params["block_products"]["value"] == 32 and "blocks of 32" in hdr
+    assert params["fraction_bits"]["value"] == 13 and "13 fraction bits" in hdr
+
+
+# ---- host builds of the kernels' rounding routines -------------------------
+def _u32(n, rng):
+    return rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+
+
+def _edge_patterns():
+    e = np.arange(256, dtype=np.uint32) << 23
+    frac = np.array([0, 1, 2, 0x1000, 0xFFF, 0x1001, 0x2000, 0x8000, 0x7FFF, 0x8001, 0x18000,
+                     0x400000, 0x7FFFFF, 0x7FE000, 0x7FF000, 0x7FEFFF], dtype=np.uint32)
+    pats = (e[:, None] | frac[None, :]).ravel()
+    return np.concatenate([pats, pats | np.uint32(0x80000000)])
+
+
+def test_host_bf16_and_f16_rounding(lib):
+    rng = np.random.default_rng(0)
+    f = np.concatenate([_u32(200000, rng), _edge_patterns()])
+    fl = f.view(np.float32)
+    nan = np.isnan(fl)
+    bf = torch.from_numpy(fl.copy()).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    want_bf = np.where(nan, np.uint16(0x7FFF), bf)
+    with np.errstate(all="ignore"):
+        h = fl.astype(np.float16).view(np.uint16)
+    want_h = np.where(nan, np.uint16(0x7FFF), h)
+    lib.emu_host_f32_to_bf16.restype = ctypes.c_uint16
+    lib.emu_host_f32_to_f16.restype = ctypes.c_uint16
+    lib.emu_host_f32_to_bf16.argtypes = [ctypes.c_uint32]
+    lib.emu_host_f32_to_f16.argtypes = [ctypes.c_uint32]
+    got_bf = np.array([lib.emu_host_f32_to_bf16(int(v)) for v in f], dtype=np.uint16)
+    got_h = np.array([lib.emu_host_f32_to_f16(int(v)) for v in f], dtype=np.uint16)
+    assert np.array_equal(got_bf, want_bf)
+    assert np.array_equal(got_h, want_h)
+
+
+def test_host_mul_and_epilogue(lib):
+    rng = np.random.default_rng(1)
+    a = np.concatenate([_u32(100000, rng), _edge_patterns()])
+    b = np.concatenate([_u32(100000, rng), _edge_patterns()[::-1]])
+    # products near the subnormal / overflow boundaries
+    b[:20000] = (b[:20000] & np.uint32(0x807FFFFF)) | ((rng.integers(0, 40, 20000) << 23).astype(np.uint32))
+    for f in (lib.emu_host_mul_f32, lib.emu_host_epilogue_f32):
+        f.restype = ctypes.c_uint32
+        f.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    fa, fb = a.view(np.float32), b.view(np.float32)
+    with np.errstate(all="ignore"):
+        prod64 = fa.astype(np.float64) * fb.astype(np.float64)
+        mul = (fa * fb)
+    want_mul = np.where(np.isnan(mul), np.uint32(0x7FFFFFFF), mul.view(np.uint32))
+    with np.errstate(all="ignore"):
+        epi = prod64.astype(np.float32)
+    epi = np.where(prod64 == 0, np.float32(0), epi)
+    want_epi = np.where(np.isnan(epi), np.uint32(0x7FFFFFFF), epi.view(np.uint32))
+    got_mul = np.array([lib.emu_host_mul_f32(int(x), int(y)) for x, y in zip(a, b)], dtype=np.uint32)
+    got_epi = np.array([lib.emu_host_epilogue_f32(int(x), int(y)) for x, y in zip(a, b)], dtype=np.uint32)
+    assert np.array_equal(got_mul, want_mul), np.argwhere(got_mul != want_mul)[:5]
+    assert np.array_equal(got_epi, want_epi), np.argwhere(got_epi != want_epi)[:5]

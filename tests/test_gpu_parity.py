@@ -1,0 +1,222 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU
+oracle, bit for bit (tolerance 0 ULP), on seeded inputs.
+
+Covers the five workloads (the 8192^3 one at full size on sampled outputs),
+every FP8 code pair, an edge-case sweep (ragged M, K not a multiple of 32 or
+128, K = 0, more splits than k-tiles, NaN / Inf / zero / subnormal codes,
+non-power-of-two scales, every output type, accumulator output), and the
+invariants the pages state (out= buffer ignored, determinism across streams,
+padding rows independent)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_exact_fp8_amd import api
+from bit_exact_fp8_amd.inputs import (FP8_DTYPES, OUT_DTYPES, WORKLOADS, Workload, inject,
+                                      make_operands, random_codes, scale_bits)
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+
+
+def gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, stream=None, prefill=None):
+    xd = x.to(dev).view(FP8_DTYPES[xfmt])
+    wd = w.to(dev).view(FP8_DTYPES[wfmt])
+    sxd = torch.tensor([sx], dtype=torch.float32, device=dev)
+    swd = torch.tensor([sw], dtype=torch.float32, device=dev)
+    o = None
+    if prefill is not None:
+        o = torch.empty((x.shape[0], w.shape[0]), dtype=OUT_DTYPES[out], device=dev)
+        o.view(torch.uint8).fill_(prefill)
+    with torch.cuda.stream(stream or torch.cuda.current_stream(dev)):
+        y = api.scaled_mm(xd, wd.t(), sxd, swd, out_dtype=OUT_DTYPES[out], use_fast_accum=fast,
+                          split_S=S, out=o)
+        acc = api.accumulate(xd, wd, use_fast_accum=fast, split_S=S)
+    torch.cuda.synchronize(dev)
+    return bits_of(y), bits_of(acc)
+
+
+def oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1):
+    return orc.scaled_mm(x.numpy(), xfmt, w.numpy(), wfmt, scale_bits(sx), scale_bits(sw), out, fast, S,
+                         threads=THREADS)
+
+
+def assert_same(got, want, what):
+    bad = got != want
+    if bad.any():
+        idx = np.argwhere(bad)
+        i = tuple(idx[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} differ; first at {i}: "
+                             f"gpu {int(got[i]):#x} oracle {int(want[i]):#x}")
+
+
+def check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, what):
+    note(f"[gpu] {what}: M={x.shape[0]} N={w.shape[0]} K={x.shape[1]} {xfmt}x{wfmt} "
+         f"fast={fast} S={S} out={out}")
+    y, acc = gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out, fast, S)
+    acc_o, y_o = oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out, fast, S)
+    assert_same(acc, acc_o, what + " accumulator")
+    assert_same(y, y_o, what + " output")
+
+
+# ---- the workloads -------------------------------------------------------------
+@pytest.mark.parametrize("name,seed", [
+    ("tiny", 0), ("tiny", 1), ("tiny", 2),
+    ("proj_64x5760x1920", 0), ("proj_64x5760x1920", 1),
+    ("slow_256x4096x4096", 0),
+    ("splitk_16x256x65536_s8", 0), ("splitk_16x256x65536_s8", 1), ("splitk_16x256x65536_s8", 2),
+])
+def test_workload_full(dev, orc, name, seed):
+    wl = WORKLOADS[name]
+    x, w = make_operands(wl, seed)
+    check(dev, orc, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S,
+          f"{name} seed {seed}")
+
+
+def test_mixed_8192_sampled(dev, orc):
+    """Full-size 8192^3 e4m3 x e5m2 run, compared on sampled outputs that the
+    oracle computes one by one: random points plus the corners and tile
+    boundaries."""
+    wl = WORKLOADS["mixed_8192"]
+    x, w = make_operands(wl, 0)
+    note("[gpu] mixed_8192 seed 0: full-size run")
+    y, acc = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S)
+    rng = np.random.default_rng(0)
+    ms = list(rng.integers(0, wl.M, 3000)) + [0, 0, wl.M - 1, wl.M - 1, 63, 64, 127, 128, 4095, 4096]
+    ns = list(rng.integers(0, wl.N, 3000)) + [0, wl.N - 1, 0, wl.N - 1, 127, 128, 63, 64, 4096, 4095]
+    ms, ns = np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+    acc_o, y_o = orc.points(x.numpy(), wl.xfmt, w.numpy(), wl.wfmt, ms, ns, scale_bits(wl.scale_x),
+                            scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S)
+    assert_same(acc[ms, ns], acc_o, "mixed_8192 accumulator")
+    assert_same(y[ms, ns], y_o, "mixed_8192 output")
+
+
+# ---- every code pair ------------------------------------------------------------
+@pytest.mark.parametrize("xfmt,wfmt", [("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn")])
+def test_every_code_pair(dev, orc, xfmt, wfmt):
+    K = 16
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    x = torch.zeros((256, K), dtype=torch.uint8)
+    w = torch.zeros((256, K), dtype=torch.uint8)
+    x[:, 3] = codes
+    w[:, 3] = codes
+    for out in ("bf16", "fp16", "fp32"):
+        check(dev, orc, x, xfmt, w, wfmt, 1 / 3, 0.1, out, True, 1, f"code pairs {xfmt}x{wfmt}")
+
+
+# ---- edge-case sweep --------------------------------------------------------------
+def _edge_case(seed):
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator().manual_seed(seed)
+    xfmt, wfmt = [("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn")][seed % 3]
+    M = int(rng.choice([1, 3, 16, 17, 33, 64, 70, 129]))
+    N = int(rng.choice([16, 32, 48, 80, 144, 272]))
+    K = int(rng.choice([0, 16, 32, 48, 112, 128, 144, 400, 1040, 2064]))
+    fast = bool(rng.integers(0, 2))
+    S = int(rng.choice([1, 1, 2, 3, 5, 17]))
+    out = str(rng.choice(["bf16", "fp16", "fp32"]))
+    x = random_codes((M, K), xfmt, gen, finite=True)
+    w = random_codes((N, K), wfmt, gen, finite=True)
+    x = inject(x, xfmt, 0.2, 0.1, gen)
+    w = inject(w, wfmt, 0.2, 0.1, gen)
+    if seed % 4 == 0 and K:  # a few NaN / Inf codes
+        for _ in range(3):
+            if xfmt == "e5m2":
+                x[rng.integers(0, M), rng.integers(0, K)] = int(rng.choice([0x7C, 0xFC, 0x7E]))
+            else:
+                x[rng.integers(0, M), rng.integers(0, K)] = int(rng.choice([0x7F, 0xFF]))
+            if wfmt == "e5m2":
+                w[rng.integers(0, N), rng.integers(0, K)] = int(rng.choice([0x7C, 0xFC, 0x7D]))
+            else:
+                w[rng.integers(0, N), rng.integers(0, K)] = 0x7F
+    sx = float(rng.choice([1 / 64, 0.1, -1 / 3, 3.0e-30, 2.0 ** -140, 65504.0]))
+    sw = float(rng.choice([1 / 32, 1 / 3, 7.0, -0.3]))
+    return x, xfmt, w, wfmt, sx, sw, out, fast, S
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_edge_cases(dev, orc, seed):
+    x, xfmt, w, wfmt, sx, sw, out, fast, S = _edge_case(seed)
+    check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, f"edge case {seed}")
+
+
+@pytest.mark.parametrize("fast,S", [(True, 1), (False, 1), (True, 4), (False, 3)])
+def test_large_tiles(dev, orc, fast, S):
+    """Sizes that select the 64x128 and 32x64 workgroup tiles, with ragged edges."""
+    wl = Workload("t", 1040, 4112, 160, zero_frac=0.05, subnormal_frac=0.05)
+    x, w = make_operands(wl, 3)
+    check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.1, 1 / 3, "bf16", fast, S, f"large tiles fast={fast} S={S}")
+
+
+# ---- invariants -------------------------------------------------------------------
+def test_out_buffer_is_ignored(dev):
+    """The result does not depend on what the output buffer held (validation
+    page, scope table row 'Epilogue')."""
+    x, w = make_operands(WORKLOADS["tiny"], 5)
+    ys = [gpu_run(dev, x, "e4m3fn", w, "e4m3fn", 0.1, 0.3, "bf16", True, 1, prefill=p)[0]
+          for p in (0x00, 0xFF, 0x7F)]
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+def test_deterministic_across_streams(dev):
+    """The same call twice, on two different streams, gives the same bits
+    (validation page: deterministic under scheduling perturbation)."""
+    wl = WORKLOADS["splitk_16x256x65536_s8"]
+    x, w = make_operands(wl, 4)
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    a = gpu_run(dev, x, "e4m3fn", w, "e4m3fn", wl.scale_x, wl.scale_w, "bf16", True, 8, stream=s1)
+    b = gpu_run(dev, x, "e4m3fn", w, "e4m3fn", wl.scale_x, wl.scale_w, "bf16", True, 8, stream=s2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_padding_rows_do_not_change_other_rows(dev):
+    """Padding M changes no other row (user guide section 7)."""
+    x, w = make_operands(WORKLOADS["proj_64x5760x1920"], 6, N=256)
+    gen = torch.Generator().manual_seed(6)
+    pad = random_codes((37, x.shape[1]), "e4m3fn", gen)
+    y0, a0 = gpu_run(dev, x, "e4m3fn", w, "e4m3fn", 1 / 64, 1 / 32)
+    y1, a1 = gpu_run(dev, torch.cat([x, pad]), "e4m3fn", w, "e4m3fn", 1 / 64, 1 / 32)
+    assert np.array_equal(y0, y1[:x.shape[0]]) and np.array_equal(a0, a1[:x.shape[0]])
+
+
+def test_strided_rows(dev, orc):
+    """Operands whose rows are longer than K (ldx, ldw > K)."""
+    x, w = make_operands(WORKLOADS["tiny"], 7, K=512)
+    K = 208
+    xs = x.to(dev)[:, :K].view(torch.float8_e4m3fn)
+    ws = w.to(dev)[:, :K].view(torch.float8_e4m3fn)
+    sx = torch.tensor([0.1], device=dev)
+    sw = torch.tensor([0.2], device=dev)
+    y = api.scaled_mm(xs, ws.t(), sx, sw, out_dtype=torch.float16, use_fast_accum=False)
+    torch.cuda.synchronize(dev)
+    acc_o, y_o = oracle_run(orc, x[:, :K].contiguous(), "e4m3fn", w[:, :K].contiguous(), "e4m3fn", 0.1, 0.2,
+                            "fp16", False, 1)
+    assert_same(bits_of(y), y_o, "strided rows")
