@@ -92,6 +92,21 @@ def cpu_baseline(wl, x, w, y_gpu, budget_s: float):
             "gpu_bit_exact_on_sample": same}
 
 
+def copy_reference(mib: int):
+    """A plain device-to-device copy of a known size: reads and writes
+    mib MiB once each.  Profiling it gives the scale of the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) for the same run conditions."""
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_reference_bytes": n, "dispatches": 3}), flush=True)
+
+
 def output_bits(t):
     t = t.cpu()
     if t.dtype == torch.float32:
@@ -108,7 +123,13 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
