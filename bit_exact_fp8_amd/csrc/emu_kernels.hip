@@ -12,7 +12,10 @@
 // How one block is computed here, per output (m, n):
 //
 //  pass 1  E from packed 16-bit exponent planes: g = ea + eb with one
-//          v_pk_add_u16 per two products, a running v_pk_max_u16.
+//          v_pk_add_u16 per two products; the planes are biased so that
+//          every sum is a positive normal binary16 pattern, whose order is
+//          the integer order, and one v_pk_maximum3_f16 folds two pairs
+//          into the running maximum.
 //  pass 2  with C = 1.5 * 2^(E-13+23), a binary32 fma in round-toward-zero
 //          mode, fma(|a|, |b|, C), returns exactly C + trunc(|a*b| / 2^(E-13))
 //          * 2^(E-13): the product is exact inside the fma, C pins the
@@ -24,7 +27,8 @@
 //  c       the same fma turns c into its truncated magnitude.
 //  block   T = signed sum (< 2^21, exact in an int); binary32(T) is exact and
 //          clearing its 10 low mantissa bits cuts it toward zero to 14
-//          significant bits; ldexp by E-13 gives the new c (exact).
+//          significant bits; a multiplication by 2^(E-13), whose bits come
+//          from C's, gives the new c (exact).
 //
 // Round-toward-zero is set once per wave at kernel entry.  Every floating
 // point instruction whose rounding matters is written as inline assembly
@@ -53,20 +57,31 @@ constexpr int CHUNK = 128;       // slow-accumulation restart
 constexpr int A_STRIDE = KB + 4; // floats per LDS row of the value plane (16 B pad)
 constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent / sign planes
 
-// Exponent plane biases: g + 127 = (ea + 64) + (eb + 63), so the biased block
-// maximum is directly comparable with the binary32 exponent field of c.  A
-// zero product has a plane value of 0 on at least one side, so its biased
-// sum is at most 15 + 63 = 78, below every real product (g >= -20 -> 107) and
-// every nonzero c (|c| >= 2^-33 -> 94).
+// Exponent planes (one u16 per code).  A nonzero code stores
+// ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
+// bias 64 for x, 63 for w, so that a product's plane sum is
+// (g + 127) + 0x400: a positive normal binary16 pattern (the block maximum
+// can use binary16 maximum instructions, whose order on such patterns is the
+// integer order) whose low 9 bits are g + 127, directly comparable with the
+// binary32 exponent field of c.  A zero code stores ZERO_PLANE = 0x208: a
+// zero product's sum is then at most 0x208 + 0x200 + 79 = 0x400 + 87, below
+// every real product (g >= -20, i.e. 0x400 + 107) and every nonzero c
+// (|c| >= 2^-33, i.e. 0x400 + 94), and at least 0x400 + 16, which keeps the
+// quantum 2^(E-13) a normal binary32 value.
 constexpr uint32_t X_EBIAS = 64;
 constexpr uint32_t W_EBIAS = 63;
+constexpr uint32_t ZERO_PLANE = 0x208u;
+constexpr uint32_t SUM_OFFSET = 0x400u;
 // C = 1.5 * 2^(E + 10) has exponent field (E + 127) + 10 and fraction 0x400000.
+// (M << 23) drops M's bit 9 and above, so the 0x400 offset of the maximum
+// vanishes from C.
 constexpr uint32_t C_OFFSET = (10u << 23) | 0x400000u;
-// q = E - 13 = (E + 127) - 140; C's exponent field is (E + 127) + 10.
-constexpr int Q_FROM_CFIELD = 150;
+// 2^q with q = E - 13 has exponent field (E + 127) - 13 = C's field - 23.
+constexpr uint32_t POW2Q_FROM_C = (23u << 23) | 0x400000u;
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef short s2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_add_u16(uint32_t a, uint32_t b)
 {
@@ -77,6 +92,50 @@ __device__ __forceinline__ uint32_t pk_add_u16(uint32_t a, uint32_t b)
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
 {
     us2 r = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// max(a, b, c) per 16-bit half, on positive normal binary16 patterns
+__device__ __forceinline__ uint32_t pk_max3_h(uint32_t a, uint32_t b, uint32_t c)
+{
+    h2 r = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b)), __builtin_bit_cast(h2, c));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// min(a, 1) per 16-bit half (written out: the compiler would unpack it)
+__device__ __forceinline__ uint32_t pk_min1_u16(uint32_t a)
+{
+    uint32_t r;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "s"(0x00010001u));
+    return r;
+}
+
+// max(lo16(g), hi16(g), lo16(e)), valid in the low 16 bits
+__device__ __forceinline__ uint32_t max3_lo_hi_u16(uint32_t g, uint32_t e)
+{
+    uint32_t r;
+    asm("v_max3_u16 %0, %1, %1, %2 op_sel:[0,1,0,0]" : "=v"(r) : "v"(g), "v"(e));
+    return r;
+}
+
+// (a.lo * b.lo + a.hi * b.hi) as signed 16-bit products, from zero
+__device__ __forceinline__ int dot2_i16_from0(uint32_t a, uint32_t b)
+{
+    int r;
+    asm("v_dot2_i32_i16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c)
+{
+    us2 r = __builtin_bit_cast(us2, a) * __builtin_bit_cast(us2, b) + __builtin_bit_cast(us2, c);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, uint32_t sh)
+{
+    us2 r = __builtin_bit_cast(us2, a) >> (us2){(unsigned short)sh, (unsigned short)sh};
     return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -131,6 +190,15 @@ __device__ __forceinline__ uint32_t fma_abs_rz(float a, float b, uint32_t c, uin
     return r;
 }
 
+// a * b where the product is exact (a power of two times a value of at most
+// 14 significant bits, in the normal range), in any mode.
+__device__ __forceinline__ uint32_t mul_exact(uint32_t a, uint32_t b, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b), "s"(tok));
+    return r;
+}
+
 // a + b in the current (round-to-nearest-even) mode.
 __device__ __forceinline__ uint32_t add_rn(uint32_t a, uint32_t b, uint32_t tok)
 {
@@ -140,64 +208,64 @@ __device__ __forceinline__ uint32_t add_rn(uint32_t a, uint32_t b, uint32_t tok)
 }
 
 // ---- FP8 decoding -----------------------------------------------------------
-// A code becomes (signed binary32 value, biased field exponent or 0 for a
-// zero, 16-bit sign mask 0xFFFE or 0).  NaN / Inf codes decode like zeros;
-// outputs they touch are overwritten by the specials rule.  Field exponents
-// of subnormals are emin (validation page, claims table).
-template <int FMT, uint32_t EBIAS>
-__device__ __forceinline__ void decode_code(uint32_t code, float &val, uint32_t &e, uint32_t &smask)
-{
-    const uint32_t s = code >> 7;
-    uint32_t M;
-    int ex;
-    bool special;
-    if (FMT == FMT_E4M3) {
-        const uint32_t ef = (code >> 3) & 15u, mf = code & 7u;
-        special = (code & 0x7Fu) == 0x7Fu;
-        ex = ef ? (int)ef - 7 : -6;
-        M = ef ? (8u | mf) : mf;
-    } else {
-        const uint32_t ef = (code >> 2) & 31u, mf = code & 3u;
-        special = ef == 31u;
-        ex = ef ? (int)ef - 15 : -14;
-        M = ef ? ((4u | mf) << 1) : (mf << 1);
-    }
-    const bool zero = special || M == 0;
-    // M * 2^(ex - 3): exact conversion of a 4-bit integer and an exact scaling
-    const float mag = __builtin_ldexpf((float)M, ex - 3);
-    val = zero ? 0.0f : (s ? -mag : mag);
-    e = zero ? 0u : (uint32_t)(ex + (int)EBIAS);
-    smask = s ? 0xFFFEu : 0u;
-}
-
-// Any NaN (E4M3) or Inf/NaN (E5M2) code among four packed codes.
+// Four codes of a row (one 32-bit word, k ascending from the low byte) become
+//   four signed binary32 values (exact hardware conversions, subnormals
+//   included),
+//   two exponent-plane pairs (u16 per code, see the plane constants above;
+//   subnormals take the field exponent emin, validation page claims table),
+//   two sign-mask pairs (u16 per code, 0xFFFF for a negative code, else 0).
+// NaN / Inf codes decode to something finite or not; outputs they touch are
+// overwritten by the specials rule, so their lanes' values do not matter.
 template <int FMT>
-__device__ __forceinline__ uint32_t has_special(uint32_t v)
+__device__ __forceinline__ void cvt4(uint32_t w, float &v0, float &v1, float &v2, float &v3)
 {
-    if (FMT == FMT_E4M3) return ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
-    return ((v & 0x7C7C7C7Cu) + 0x04040404u) & 0x80808080u;
+    if (FMT == FMT_E4M3) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+        v0 = lo[0]; v1 = lo[1]; v2 = hi[0]; v3 = hi[1];
+    } else {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+        v0 = lo[0]; v1 = lo[1]; v2 = hi[0]; v3 = hi[1];
+    }
 }
 
-// Decode 16 consecutive codes of one row into the LDS planes; returns the
-// special flag of the chunk.
+// Exponent-plane pair of two codes held as [code0, 0, code1, 0].
 template <int FMT, uint32_t EBIAS>
-__device__ __forceinline__ uint32_t decode_chunk(uint4 raw, float *va, uint32_t *ve, uint32_t *vs)
+__device__ __forceinline__ uint32_t plane_pair(uint32_t p)
+{
+    constexpr uint32_t FBIAS = (FMT == FMT_E4M3) ? 7u : 15u;
+    constexpr uint32_t SH = (FMT == FMT_E4M3) ? 3u : 2u;
+    // nonzero: max(ef, 1) - FBIAS + 0x200 + EBIAS = (max(ef,1) + K) * 1 + ZERO_PLANE
+    constexpr uint32_t K = 0x200u + EBIAS - FBIAS - ZERO_PLANE;
+    const uint32_t mag = p & 0x007F007Fu;
+    const uint32_t ef = pk_shr_u16(mag, SH);
+    const uint32_t nz = pk_min1_u16(mag);
+    const uint32_t pl = pk_add_u16(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                                       __builtin_bit_cast(us2, ef), (us2){1, 1})),
+                                   K | (K << 16));
+    return pk_mad_u16(pl, nz, ZERO_PLANE | (ZERO_PLANE << 16));
+}
+
+// Decode 16 consecutive codes of one row into the LDS planes.
+template <int FMT, uint32_t EBIAS>
+__device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve, uint32_t *vs)
 {
     const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t flag = 0;
     float v[16];
     uint32_t ep[8], sp[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        flag |= has_special<FMT>(words[q]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t e0, e1, s0, s1;
-            decode_code<FMT, EBIAS>((words[q] >> (16 * h)) & 0xFFu, v[4 * q + 2 * h], e0, s0);
-            decode_code<FMT, EBIAS>((words[q] >> (16 * h + 8)) & 0xFFu, v[4 * q + 2 * h + 1], e1, s1);
-            ep[2 * q + h] = e0 | (e1 << 16);
-            sp[2 * q + h] = s0 | (s1 << 16);
-        }
+        const uint32_t w = words[q];
+        cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        ep[2 * q] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
+        ep[2 * q + 1] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+        // v_perm selectors 8..11 replicate the top bit of bytes 1, 3 of the
+        // second source and bytes 1, 3 of the first: with (w << 8, w) these
+        // are the signs of codes 1, 3, 0, 2.
+        const uint32_t t = w << 8;
+        sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
+        sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -207,7 +275,14 @@ __device__ __forceinline__ uint32_t decode_chunk(uint4 raw, float *va, uint32_t 
         *reinterpret_cast<uint4 *>(ve + 4 * q) = make_uint4(ep[4 * q], ep[4 * q + 1], ep[4 * q + 2], ep[4 * q + 3]);
         *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
     }
-    return flag;
+}
+
+// Any NaN (E4M3) or Inf/NaN (E5M2) code among four packed codes.
+template <int FMT>
+__device__ __forceinline__ uint32_t has_special(uint32_t v)
+{
+    if (FMT == FMT_E4M3) return ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    return ((v & 0x7C7C7C7Cu) + 0x04040404u) & 0x80808080u;
 }
 
 template <int FMT>
@@ -348,14 +423,18 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
             const int idx = t + q * NT;
             if (idx < NCHUNK) {
                 const int r = idx >> 1, half = idx & 1;
-                if (r < BM)
-                    myflag[q] |= decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                           xe + r * P_STRIDE + 8 * half,
-                                                           xs + r * P_STRIDE + 8 * half);
-                else
-                    myflag[q] |= decode_chunk<WF, W_EBIAS>(raw[q], wa + (r - BM) * A_STRIDE + 16 * half,
-                                                           we + (r - BM) * P_STRIDE + 8 * half,
-                                                           wsg + (r - BM) * P_STRIDE + 8 * half);
+                if (r < BM) {
+                    myflag[q] |= has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
+                                 has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
+                    decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half, xe + r * P_STRIDE + 8 * half,
+                                              xs + r * P_STRIDE + 8 * half);
+                } else {
+                    myflag[q] |= has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
+                                 has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
+                    decode_chunk<WF, W_EBIAS>(raw[q], wa + (r - BM) * A_STRIDE + 16 * half,
+                                              we + (r - BM) * P_STRIDE + 8 * half,
+                                              wsg + (r - BM) * P_STRIDE + 8 * half);
+                }
             }
         }
         __syncthreads();
@@ -381,10 +460,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     uint32_t g = gmax[i][j];
-                    g = pk_max_u16(g, pk_add_u16(ea[i].x, eb[j].x));
-                    g = pk_max_u16(g, pk_add_u16(ea[i].y, eb[j].y));
-                    g = pk_max_u16(g, pk_add_u16(ea[i].z, eb[j].z));
-                    g = pk_max_u16(g, pk_add_u16(ea[i].w, eb[j].w));
+                    g = pk_max3_h(g, pk_add_u16(ea[i].x, eb[j].x), pk_add_u16(ea[i].y, eb[j].y));
+                    g = pk_max3_h(g, pk_add_u16(ea[i].z, eb[j].z), pk_add_u16(ea[i].w, eb[j].w));
                     gmax[i][j] = g;
                 }
         }
@@ -397,12 +474,13 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
 #pragma unroll
             for (int j = 0; j < RN; ++j) {
                 const uint32_t g = gmax[i][j];
-                uint32_t e = max(g & 0xFFFFu, g >> 16);
-                e = max(e, (c[i][j] >> 23) & 0xFFu);
-                Cb[i][j] = (e << 23) + C_OFFSET;
+                const uint32_t ec = ((c[i][j] >> 23) & 0xFFu) | SUM_OFFSET;
+                // only the low 9 bits of the maximum reach C
+                Cb[i][j] = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
                 const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
-                const int uc = (int)(rc & 0xFFFFu);
-                acc[i][j] = (c[i][j] >> 31) ? -uc : uc;
+                // (+-1, 0) applies c's sign to the truncated magnitude in the low half
+                const uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                acc[i][j] = dot2_i16_from0(rc, sc);
             }
 
         // pass 2: truncated terms, signs, accumulation
@@ -430,8 +508,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
                     const uint32_t r2 = fma_abs_rz(av[i].z, bv[j].z, C, tok);
                     const uint32_t r3 = fma_abs_rz(av[i].w, bv[j].w, C, tok);
                     int a = acc[i][j];
-                    a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), (sa[i].x ^ sb[j].x) + 0x00010001u, a);
-                    a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), (sa[i].y ^ sb[j].y) + 0x00010001u, a);
+                    a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), (sa[i].x ^ sb[j].x) | 0x00010001u, a);
+                    a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), (sa[i].y ^ sb[j].y) | 0x00010001u, a);
                     acc[i][j] = a;
                 }
         }
@@ -442,8 +520,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
 #pragma unroll
             for (int j = 0; j < RN; ++j) {
                 const uint32_t tb = __float_as_uint((float)acc[i][j]) & 0xFFFFFC00u;
-                const int q = (int)(Cb[i][j] >> 23) - Q_FROM_CFIELD;
-                c[i][j] = __float_as_uint(__builtin_ldexpf(__uint_as_float(tb), q));
+                c[i][j] = mul_exact(tb, Cb[i][j] - POW2Q_FROM_C, tok);
             }
 
         // slow accumulation: add the chunk result every 128 K, in K order
