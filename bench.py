@@ -123,6 +123,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile", type=int, default=-1, help="force a tile configuration (tuning)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -151,6 +152,8 @@ def main():
     ws_bytes = api.workspace_bytes(wl.M, wl.N, wl.K, wl.split_S, wl.fast)
     wsbuf = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     lib = api._lib()
+    if args.tile >= 0:
+        api.force_tile(args.tile)
     stream = torch.cuda.current_stream(dev)
     call_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
                  wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), out.data_ptr(), api.OUT_DTYPE[out.dtype],

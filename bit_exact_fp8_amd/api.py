@@ -62,12 +62,26 @@ def _lib():
     lib.emu_status_string.restype = ctypes.c_char_p
     lib.emu_last_error_message.restype = ctypes.c_char_p
     lib.emu_abi_version.restype = i32
+    lib.emu_debug_force_tile.argtypes = [i32]
+    lib.emu_debug_force_tile.restype = i32
     _LIB = lib
     return lib
 
 
 def abi_version() -> int:
     return _lib().emu_abi_version()
+
+
+TILE_CONFIGS = ("64x128", "64x64", "32x64", "32x32", "16x16_g2", "16x16_g4")
+
+
+def force_tile(cfg: int) -> int:
+    """Force the main kernel's tile configuration (index into TILE_CONFIGS,
+    -1 for the automatic choice).  Returns the previous setting."""
+    prev = _lib().emu_debug_force_tile(int(cfg))
+    if prev == -2:
+        raise ValueError(f"invalid tile configuration {cfg}")
+    return prev
 
 
 def _check(status: int):

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <atomic>
 #include <string>
 
 #include "../../include/emu_fp8gemm.h"
@@ -51,16 +53,36 @@ Plan make_plan(int64_t K, int S)
     return p;
 }
 
-// Pick the largest workgroup tile that still gives the GPU enough workgroups.
+// Tile configuration forced through emu_debug_force_tile (-1: automatic).
+std::atomic<int> g_forced_tile{-1};
+
+// Pick the tile configuration with the best expected throughput: its
+// measured steady-state efficiency on MI355X (fraction of the integer-VALU
+// roofline once the GPU holds at least two waves per SIMD) scaled down by
+// how far the launch falls short of 2 waves on each of the 1,024 SIMDs.
 int choose_tile(int64_t M, int64_t N, int S)
 {
-    const int order[] = {emu::TILE_64x128, emu::TILE_32x64, emu::TILE_16x16};
-    for (int cfg : order) {
-        const emu::TileShape t = emu::tile_shape(cfg);
-        const int64_t wgs = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * S;
-        if (wgs >= 512) return cfg;
+    const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    if (forced >= 0) return forced;
+    struct Cand {
+        int cfg;
+        double eff;
+    };
+    const Cand cands[] = {{emu::TILE_64x64, 0.90}, {emu::TILE_64x128, 0.87}, {emu::TILE_32x64, 0.60},
+                          {emu::TILE_32x32, 0.60}, {emu::TILE_16x16_G2, 0.27}, {emu::TILE_16x16_G4, 0.15}};
+    int best = emu::TILE_16x16_G4;
+    double best_est = -1.0;
+    for (const Cand &c : cands) {
+        const emu::TileShape t = emu::tile_shape(c.cfg);
+        const double waves = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn) * S *
+                             (t.threads / 64);
+        const double est = c.eff * (waves >= 2048.0 ? 1.0 : waves / 2048.0);
+        if (est > best_est) {
+            best_est = est;
+            best = c.cfg;
+        }
     }
-    return emu::TILE_16x16;
+    return best;
 }
 
 emu_status check_common(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w,
@@ -228,6 +250,12 @@ const char *emu_status_string(emu_status status)
 const char *emu_last_error_message(void) { return g_last_error.c_str(); }
 
 int emu_abi_version(void) { return EMU_ABI_VERSION; }
+
+int emu_debug_force_tile(int cfg)
+{
+    if (cfg < -1 || cfg >= emu::TILE_COUNT) return -2;
+    return g_forced_tile.exchange(cfg);
+}
 
 uint32_t emu_host_mul_f32(uint32_t a, uint32_t b) { return emu::mul_f32(a, b); }
 uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha) { return emu::canon_f32(emu::epilogue_f32(acc, alpha)); }

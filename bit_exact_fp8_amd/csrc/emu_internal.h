@@ -38,9 +38,18 @@ struct CombineParams {
     const float *scale_x, *scale_w;
 };
 
-// Tile configurations of the main kernel (rows x cols per workgroup, and
-// per thread).
-enum TileConfig : int { TILE_64x128 = 0, TILE_32x64 = 1, TILE_16x16 = 2, TILE_COUNT = 3 };
+// Tile configurations of the main kernel: rows x cols per workgroup; per
+// thread 4x8, 4x4, 2x4, 2x2 outputs, or one output chain shared by 2 or 4
+// lanes (G2, G4).
+enum TileConfig : int {
+    TILE_64x128 = 0,
+    TILE_64x64 = 1,
+    TILE_32x64 = 2,
+    TILE_32x32 = 3,
+    TILE_16x16_G2 = 4,
+    TILE_16x16_G4 = 5,
+    TILE_COUNT = 6
+};
 
 struct TileShape {
     int bm, bn, threads;

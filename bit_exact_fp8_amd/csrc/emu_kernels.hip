@@ -144,6 +144,18 @@ __device__ __forceinline__ int dot2_i16(uint32_t a, uint32_t b, int c)
     return __builtin_amdgcn_sdot2(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b), c, false);
 }
 
+// Exchange with the partner lane inside each quad: lane ^ 1 (quad_perm
+// [1,0,3,2]) and lane ^ 2 (quad_perm [2,3,0,1]).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+
 // ---- floating-point mode control -----------------------------------------
 // MODE register bits [1:0]: binary32 rounding (0 nearest even, 3 toward zero).
 __device__ __forceinline__ uint32_t mode_round_toward_zero()
@@ -348,13 +360,18 @@ __device__ __forceinline__ void store_output(const MainParams &p, int64_t m, int
 // Minimum waves per SIMD the register allocation must allow for a thread tile.
 template <int RM, int RN>
 struct WavesPerSimd {
-    static constexpr int value = (RM * RN >= 32) ? 2 : 4;
+    static constexpr int value = (RM * RN >= 16) ? 2 : 4;
 };
 
-template <int XF, int WF, int BM, int BN, int RM, int RN, bool FAST>
-__global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
+// G lanes share each output chain (G = 1, 2 or 4): lane g of a chain takes
+// the g-th of G equal slices of every 32-product block; the block maximum
+// and the block sum are combined across the G lanes with quad DPP moves, and
+// every lane of the chain then carries the same accumulator.
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST>
+__global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
 {
-    constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN;
+    static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
+    constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per block: two per row
     constexpr int CPT = (NCHUNK + NT - 1) / NT;
 
@@ -367,7 +384,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
     __shared__ uint32_t flags[BM + BN];
 
     const int t = threadIdx.x;
-    const int tn = t % TN, tm = t / TN;
+    const int lane_g = t % G, slot = t / G;
+    const int tn = slot % TN, tm = slot / TN;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int split = blockIdx.z;
     const int64_t k_begin = (int64_t)split * p.split_len;
@@ -447,7 +465,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
 #pragma unroll
             for (int j = 0; j < RN; ++j) gmax[i][j] = 0u;
 #pragma unroll 1
-        for (int q4 = 0; q4 < KP / 4; ++q4) {
+        for (int q4 = lane_g * (KP / 4 / G); q4 < (lane_g + 1) * (KP / 4 / G); ++q4) {
             uint4 ea[RM], eb[RN];
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -466,6 +484,19 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
                 }
         }
 
+        if (G >= 2) {
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    uint32_t g = gmax[i][j];
+                    if (G == 2) g = pk_max3_h(g, quad_xor1(g), g);
+                    if (G == 4) g = pk_max3_h(g, quad_xor1(g), quad_xor2(g));
+                    if (G == 4) g = pk_max3_h(g, quad_xor1(g), g);
+                    gmax[i][j] = g;
+                }
+        }
+
         // block prologue: C and the truncated incoming accumulator
         uint32_t Cb[RM][RN];
         int acc[RM][RN];
@@ -479,13 +510,14 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
                 Cb[i][j] = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
                 const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
                 // (+-1, 0) applies c's sign to the truncated magnitude in the low half
-                const uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                if (G > 1) sc = (lane_g == 0) ? sc : 0u;  // c enters the block sum once
                 acc[i][j] = dot2_i16_from0(rc, sc);
             }
 
         // pass 2: truncated terms, signs, accumulation
 #pragma unroll 1
-        for (int k4 = 0; k4 < KB / 4; ++k4) {
+        for (int k4 = lane_g * (KB / 4 / G); k4 < (lane_g + 1) * (KB / 4 / G); ++k4) {
             float4 av[RM], bv[RN];
             uint2 sa[RM], sb[RN];
 #pragma unroll
@@ -510,6 +542,18 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
                     int a = acc[i][j];
                     a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), (sa[i].x ^ sb[j].x) | 0x00010001u, a);
                     a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), (sa[i].y ^ sb[j].y) | 0x00010001u, a);
+                    acc[i][j] = a;
+                }
+        }
+
+        if (G >= 2) {
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    int a = acc[i][j];
+                    a += (int)quad_xor1((uint32_t)a);
+                    if (G == 4) a += (int)quad_xor2((uint32_t)a);
                     acc[i][j] = a;
                 }
         }
@@ -560,7 +604,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN), (WavesPerSimd<RM, RN>::value
         for (int j = 0; j < RN; ++j) {
             const int rm = tm + i * TM, rn = tn + j * TN;
             const int64_t m = m0 + rm, n = n0 + rn;
-            if (m >= p.M || n >= p.N) continue;
+            if (m >= p.M || n >= p.N || lane_g != 0) continue;
             uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
             if (flags[rm] | flags[BM + rn])
                 a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, k_begin, k_end);
@@ -593,15 +637,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
         reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(y);
 }
 
-template <int XF, int WF, int BM, int BN, int RM, int RN>
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G>
 hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
 {
-    constexpr int NT = (BM / RM) * (BN / RN);
+    constexpr int NT = (BM / RM) * (BN / RN) * G;
     dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, S);
     if (p.fast)
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, true>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true>), grid, dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, false>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false>), grid, dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -609,9 +653,12 @@ template <int XF, int WF>
 hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
 {
     switch (cfg) {
-    case TILE_64x128: return launch_cfg<XF, WF, 64, 128, 4, 8>(p, S, stream);
-    case TILE_32x64: return launch_cfg<XF, WF, 32, 64, 2, 4>(p, S, stream);
-    case TILE_16x16: return launch_cfg<XF, WF, 16, 16, 1, 1>(p, S, stream);
+    case TILE_64x128: return launch_cfg<XF, WF, 64, 128, 4, 8, 1>(p, S, stream);
+    case TILE_64x64: return launch_cfg<XF, WF, 64, 64, 4, 4, 1>(p, S, stream);
+    case TILE_32x64: return launch_cfg<XF, WF, 32, 64, 2, 4, 1>(p, S, stream);
+    case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1>(p, S, stream);
+    case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2>(p, S, stream);
+    case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -622,8 +669,11 @@ TileShape tile_shape(int cfg)
 {
     switch (cfg) {
     case TILE_64x128: return {64, 128, 256};
+    case TILE_64x64: return {64, 64, 256};
     case TILE_32x64: return {32, 64, 256};
-    default: return {16, 16, 256};
+    case TILE_32x32: return {32, 32, 256};
+    case TILE_16x16_G2: return {16, 16, 512};
+    default: return {16, 16, 1024};
     }
 }
 

@@ -136,6 +136,17 @@ EMU_API const char *emu_last_error_message(void);
 EMU_API int emu_abi_version(void);
 
 /*
+ * Testing and tuning: force the main kernel's tile configuration for every
+ * later call in the process (cfg = -1 restores the automatic choice; valid
+ * configurations are 0 .. 5: 64x128, 64x64, 32x64, 32x32 output tiles with
+ * one lane per output, 16x16 with 2 or 4 lanes per output).  Results do not
+ * depend on the configuration.  Returns the previous setting, or -2 (and
+ * changes nothing) for an invalid cfg.  Process-wide; not for concurrent use
+ * with calls that expect the automatic choice.
+ */
+EMU_API int emu_debug_force_tile(int cfg);
+
+/*
  * Host builds of the library's own IEEE rounding routines, the same source
  * its kernels use, exported so that CPU tests can check them without a GPU.
  * All arguments and results are bit patterns.

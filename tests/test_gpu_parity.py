@@ -176,6 +176,24 @@ def test_large_tiles(dev, orc, fast, S):
     check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.1, 1 / 3, "bf16", fast, S, f"large tiles fast={fast} S={S}")
 
 
+@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("shape", [(1, 16, 48), (37, 80, 400), (70, 144, 1040)])
+def test_every_tile_config(dev, orc, cfg, shape):
+    """Every tile configuration (including 2 and 4 lanes per output) gives the
+    oracle's bits, fast and slow, unsplit and split, on ragged shapes."""
+    M, N, K = shape
+    gen = torch.Generator().manual_seed(100 + cfg)
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
+    w = inject(random_codes((N, K), "e5m2", gen), "e5m2", 0.1, 0.05, gen)
+    prev = api.force_tile(cfg)
+    try:
+        for fast, S in ((True, 1), (False, 1), (True, 3), (False, 2)):
+            check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, "bf16", fast, S,
+                  f"tile {api.TILE_CONFIGS[cfg]} {shape}")
+    finally:
+        api.force_tile(prev)
+
+
 # ---- invariants -------------------------------------------------------------------
 def test_out_buffer_is_ignored(dev):
     """The result does not depend on what the output buffer held (validation
