@@ -40,7 +40,7 @@ struct CombineParams {
 
 // Tile configurations of the main kernel: rows x cols per workgroup; per
 // thread 4x8, 4x4, 2x4, 2x2 outputs, or one output chain shared by 2 or 4
-// lanes (G2, G4).
+// lanes (G2, G4); MX: block exponent maxima on the matrix cores.
 enum TileConfig : int {
     TILE_64x128 = 0,
     TILE_64x64 = 1,
@@ -48,7 +48,9 @@ enum TileConfig : int {
     TILE_32x32 = 3,
     TILE_16x16_G2 = 4,
     TILE_16x16_G4 = 5,
-    TILE_COUNT = 6
+    TILE_64x64_MX = 6,
+    TILE_64x128_MX = 7,
+    TILE_COUNT = 8
 };
 
 struct TileShape {

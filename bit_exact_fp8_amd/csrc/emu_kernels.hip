@@ -79,7 +79,28 @@ constexpr uint32_t C_OFFSET = (10u << 23) | 0x400000u;
 // 2^q with q = E - 13 has exponent field (E + 127) - 13 = C's field - 23.
 constexpr uint32_t POW2Q_FROM_C = (23u << 23) | 0x400000u;
 
+// Exponent maximum on the matrix cores.  x codes become 2^(4*ex + 5), w codes
+// 2^(4*ew + 4), zeros 0 (bf16 "power planes").  For one quarter-block (8
+// consecutive k), sum_k of the products is S = sum of 2^(4*g_k + 9) over
+// the nonzero products: each term is exact in fp32 and
+// 2^(4G+9) <= S <= 8 * 2^(4G+9) = 2^(4G+12) for G = max g_k, so the binary32
+// exponent field of S, 4G + 136 .. 4G + 139, shifted right by 2 is exactly
+// G + 34.  This holds for any accumulation order and any faithful rounding
+// (the largest term is exact, adding nonnegative terms never goes below it
+// and 8 terms cannot reach 2^(4G+13)), so the matrix instruction's own
+// rounding cannot change the result.  A quarter with no nonzero product
+// gives S = 0, i.e. 0 after the shift, below every real product
+// (G >= -20 -> 14).  The biased block maximum is then
+// E + 127 = max over the four quarters of (S >> 25) + 93, compared with c's
+// binary32 exponent field (|c| >= 2^-33 -> 94 or more, c = 0 -> 0).
+constexpr uint32_t X_POW_OFF = 5;
+constexpr uint32_t W_POW_OFF = 4;
+constexpr uint32_t POW_TO_EB = 93;
+constexpr int PW_ROW = 8;  // words per (quarter, row) of a power plane: 8 real + 8 zero bf16
+
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short s2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -130,6 +151,12 @@ __device__ __forceinline__ int dot2_i16_from0(uint32_t a, uint32_t b)
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c)
 {
     us2 r = __builtin_bit_cast(us2, a) * __builtin_bit_cast(us2, b) + __builtin_bit_cast(us2, c);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
+{
+    us2 r = __builtin_bit_cast(us2, a) * __builtin_bit_cast(us2, b);
     return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -259,6 +286,51 @@ __device__ __forceinline__ uint32_t plane_pair(uint32_t p)
     return pk_mad_u16(pl, nz, ZERO_PLANE | (ZERO_PLANE << 16));
 }
 
+// Power-plane pair (bf16 bits of 2^(4*ex + OFF), 0 for a zero code) of two
+// codes held as [code0, 0, code1, 0]; ex is the field exponent (emin for
+// subnormals).  bf16 bits of 2^E are (E + 127) << 7, and
+// E + 127 = 4*max(ef, 1) + (OFF + 127 - 4*FBIAS).
+template <int FMT, uint32_t OFF>
+__device__ __forceinline__ uint32_t power_pair(uint32_t p)
+{
+    constexpr uint32_t FBIAS = (FMT == FMT_E4M3) ? 7u : 15u;
+    constexpr uint32_t SH = (FMT == FMT_E4M3) ? 3u : 2u;
+    constexpr uint32_t K = (OFF + 127u - 4u * FBIAS) << 7;
+    const uint32_t mag = p & 0x007F007Fu;
+    const uint32_t ef = pk_shr_u16(mag, SH);
+    const uint32_t nz = pk_min1_u16(mag);
+    const uint32_t efc = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, ef), (us2){1, 1}));
+    return pk_mul_u16(pk_mad_u16(efc, 0x02000200u, K | (K << 16)), nz);
+}
+
+// Decode 16 consecutive codes of one row into the value and sign planes and
+// the power plane (the two quarter-blocks the 16 codes cover, 8 codes each).
+template <int FMT, uint32_t OFF>
+__device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *vs, uint32_t *pq0, uint32_t *pq1)
+{
+    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[16];
+    uint32_t pp[8], sp[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = words[q];
+        cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        pp[2 * q] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
+        pp[2 * q + 1] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+        const uint32_t t = w << 8;
+        sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
+        sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
+    *reinterpret_cast<uint4 *>(pq0) = make_uint4(pp[0], pp[1], pp[2], pp[3]);
+    *reinterpret_cast<uint4 *>(pq1) = make_uint4(pp[4], pp[5], pp[6], pp[7]);
+}
+
 // Decode 16 consecutive codes of one row into the LDS planes.
 template <int FMT, uint32_t EBIAS>
 __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve, uint32_t *vs)
@@ -367,25 +439,44 @@ struct WavesPerSimd {
 // the g-th of G equal slices of every 32-product block; the block maximum
 // and the block sum are combined across the G lanes with quad DPP moves, and
 // every lane of the chain then carries the same accumulator.
-template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST>
+//
+// MX: the block maximum comes from bf16 matrix instructions (see the power
+// planes above) instead of packed VALU maxima.  Needs RM = 4, G = 1 and one
+// wave per 16 rows: the wave's 16 x (16*RN) output tile is RN 16x16
+// matrix-instruction tiles, and lane l owns rows 4*(l/16) + i and columns
+// l%16 + 16*j, the layout of v_mfma_f32_16x16x16_bf16's result.
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST, bool MX>
 __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
+    static_assert(!MX || (RM == 4 && G == 1 && BN == 16 * RN && (BM / 16) * 64 == (BM / RM) * (BN / RN)),
+                  "matrix-instruction exponents need 16-row waves with 4x RN thread tiles");
     constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per block: two per row
     constexpr int CPT = (NCHUNK + NT - 1) / NT;
 
     __shared__ __attribute__((aligned(16))) float xa[BM * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t xe[BM * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xe[MX ? 4 : BM * P_STRIDE];
     __shared__ __attribute__((aligned(16))) uint32_t xs[BM * P_STRIDE];
     __shared__ __attribute__((aligned(16))) float wa[BN * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t we[BN * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t we[MX ? 4 : BN * P_STRIDE];
     __shared__ __attribute__((aligned(16))) uint32_t wsg[BN * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
     __shared__ uint32_t flags[BM + BN];
 
     const int t = threadIdx.x;
     const int lane_g = t % G, slot = t / G;
     const int tn = slot % TN, tm = slot / TN;
+    const int wave = t >> 6, lane = t & 63;
+    // local row of chain i, local column of chain j
+    auto row_of = [&](int i) { return MX ? 16 * wave + 4 * (lane >> 4) + i : tm + i * TM; };
+    auto col_of = [&](int j) { return MX ? (lane & 15) + 16 * j : tn + j * TN; };
+
+    if (MX) {  // zero the power planes once: the upper 8 bf16 of every quarter row stay zero
+        for (int i = t; i < BM * PW_ROW; i += NT) reinterpret_cast<uint4 *>(xp)[i] = make_uint4(0, 0, 0, 0);
+        for (int i = t; i < BN * PW_ROW; i += NT) reinterpret_cast<uint4 *>(wp)[i] = make_uint4(0, 0, 0, 0);
+    }
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int split = blockIdx.z;
     const int64_t k_begin = (int64_t)split * p.split_len;
@@ -444,20 +535,63 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 if (r < BM) {
                     myflag[q] |= has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
                                  has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
-                    decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half, xe + r * P_STRIDE + 8 * half,
-                                              xs + r * P_STRIDE + 8 * half);
+                    if (MX)
+                        decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
+                                                       xs + r * P_STRIDE + 8 * half,
+                                                       xp + ((2 * half) * BM + r) * PW_ROW,
+                                                       xp + ((2 * half + 1) * BM + r) * PW_ROW);
+                    else
+                        decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
+                                                  xe + r * P_STRIDE + 8 * half, xs + r * P_STRIDE + 8 * half);
                 } else {
+                    const int rw = r - BM;
                     myflag[q] |= has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
                                  has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
-                    decode_chunk<WF, W_EBIAS>(raw[q], wa + (r - BM) * A_STRIDE + 16 * half,
-                                              we + (r - BM) * P_STRIDE + 8 * half,
-                                              wsg + (r - BM) * P_STRIDE + 8 * half);
+                    if (MX)
+                        decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
+                                                       wsg + rw * P_STRIDE + 8 * half,
+                                                       wp + ((2 * half) * BN + rw) * PW_ROW,
+                                                       wp + ((2 * half + 1) * BN + rw) * PW_ROW);
+                    else
+                        decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
+                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * P_STRIDE + 8 * half);
                 }
             }
         }
         __syncthreads();
         if (kb + KB < k_end) load_block(kb + KB);  // prefetch; latency hidden by the compute below
 
+        uint32_t Cb[RM][RN];
+        int acc[RM][RN];
+        if constexpr (MX) {
+            // pass 1 on the matrix cores: per quarter-block, S for every output
+            uint32_t smax[RM][RN];
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                const s4 a = *reinterpret_cast<const s4 *>(xp + (qb * BM + 16 * wave + (lane & 15)) * PW_ROW +
+                                                           2 * (lane >> 4));
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    const s4 b = *reinterpret_cast<const s4 *>(wp + (qb * BN + 16 * j + (lane & 15)) * PW_ROW +
+                                                               2 * (lane >> 4));
+                    const f4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < RM; ++i)
+                        smax[i][j] = qb ? max(smax[i][j], __float_as_uint(d[i])) : __float_as_uint(d[i]);
+                }
+            }
+            // block prologue: C and the truncated incoming accumulator
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    const uint32_t eb = max((smax[i][j] >> 25) + POW_TO_EB, (c[i][j] >> 23) & 0xFFu);
+                    Cb[i][j] = (eb << 23) + C_OFFSET;
+                    const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
+                    const uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                    acc[i][j] = dot2_i16_from0(rc, sc);
+                }
+        } else {
         // pass 1: E per output
         uint32_t gmax[RM][RN];
 #pragma unroll
@@ -498,8 +632,6 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         }
 
         // block prologue: C and the truncated incoming accumulator
-        uint32_t Cb[RM][RN];
-        int acc[RM][RN];
 #pragma unroll
         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -514,6 +646,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 if (G > 1) sc = (lane_g == 0) ? sc : 0u;  // c enters the block sum once
                 acc[i][j] = dot2_i16_from0(rc, sc);
             }
+        }
 
         // pass 2: truncated terms, signs, accumulation
 #pragma unroll 1
@@ -522,13 +655,13 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             uint2 sa[RM], sb[RN];
 #pragma unroll
             for (int i = 0; i < RM; ++i) {
-                av[i] = *reinterpret_cast<const float4 *>(xa + (tm + i * TM) * A_STRIDE + 4 * k4);
-                sa[i] = *reinterpret_cast<const uint2 *>(xs + (tm + i * TM) * P_STRIDE + 2 * k4);
+                av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
+                sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * P_STRIDE + 2 * k4);
             }
 #pragma unroll
             for (int j = 0; j < RN; ++j) {
-                bv[j] = *reinterpret_cast<const float4 *>(wa + (tn + j * TN) * A_STRIDE + 4 * k4);
-                sb[j] = *reinterpret_cast<const uint2 *>(wsg + (tn + j * TN) * P_STRIDE + 2 * k4);
+                bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
+                sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * P_STRIDE + 2 * k4);
             }
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -602,7 +735,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j) {
-            const int rm = tm + i * TM, rn = tn + j * TN;
+            const int rm = row_of(i), rn = col_of(j);
             const int64_t m = m0 + rm, n = n0 + rn;
             if (m >= p.M || n >= p.N || lane_g != 0) continue;
             uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
@@ -637,15 +770,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
         reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(y);
 }
 
-template <int XF, int WF, int BM, int BN, int RM, int RN, int G>
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool MX = false>
 hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
 {
     constexpr int NT = (BM / RM) * (BN / RN) * G;
     dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, S);
     if (p.fast)
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true, MX>), grid, dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false, MX>), grid, dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -659,6 +792,8 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1>(p, S, stream);
     case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2>(p, S, stream);
     case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4>(p, S, stream);
+    case TILE_64x64_MX: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, true>(p, S, stream);
+    case TILE_64x128_MX: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, true>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -673,7 +808,9 @@ TileShape tile_shape(int cfg)
     case TILE_32x64: return {32, 64, 256};
     case TILE_32x32: return {32, 32, 256};
     case TILE_16x16_G2: return {16, 16, 512};
-    default: return {16, 16, 1024};
+    case TILE_16x16_G4: return {16, 16, 1024};
+    case TILE_64x64_MX: return {64, 64, 256};
+    default: return {64, 128, 256};
     }
 }
 

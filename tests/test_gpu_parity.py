@@ -176,7 +176,7 @@ def test_large_tiles(dev, orc, fast, S):
     check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.1, 1 / 3, "bf16", fast, S, f"large tiles fast={fast} S={S}")
 
 
-@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("cfg", range(8))
 @pytest.mark.parametrize("shape", [(1, 16, 48), (37, 80, 400), (70, 144, 1040)])
 def test_every_tile_config(dev, orc, cfg, shape):
     """Every tile configuration (including 2 and 4 lanes per output) gives the
