@@ -97,25 +97,55 @@ def block(c: Fraction, prods, F):
     return trunc_to_quantum(total, Fraction(2) ** (lead - F))
 
 
-def products(xrow, xfmt, wrow, wfmt, k0, k1):
-    out = []
-    for k in range(k0, k1):
-        ka, sa, ea, va = decode(int(xrow[k]), xfmt)
-        kb, sb, eb, vb = decode(int(wrow[k]), wfmt)
-        out.append((ka, sa, ea, va, kb, sb, eb, vb))
-    return out
-
-
-def chain(xrow, xfmt, wrow, wfmt, k0, k1, B, F):
-    """Blocks of B consecutive products from k0, each stepping the accumulator."""
+def chain(xrow, xfmt, wrow, wfmt, k0, k1, B, F, ks=None):
+    """Blocks of B consecutive products (of range(k0, k1), or of the ordered
+    index list ks), each stepping the accumulator."""
+    ks = list(range(k0, k1)) if ks is None else list(ks)
     c = Fraction(0)
-    for kb in range(k0, k1, B):
+    for i in range(0, len(ks), B):
         prods = []
-        for ka, sa, ea, va, kb_, sb, eb, vb in products(xrow, xfmt, wrow, wfmt, kb, min(kb + B, k1)):
-            if ka == FIN and kb_ == FIN:
+        for k in ks[i:i + B]:
+            ka, sa, ea, va = decode(int(xrow[k]), xfmt)
+            kb, sb, eb, vb = decode(int(wrow[k]), wfmt)
+            if ka == FIN and kb == FIN:
                 prods.append((va * vb, ea + eb))
         c = block(c, prods, F)
     return c
+
+
+def split_indices(K, S, W, layout):
+    """The ordered k indices of every split.  contiguous: runs of
+    ceil(ceil(K/W)/S) tiles of width W; round-robin: tile t goes to split
+    t mod S, in increasing t."""
+    tiles = [list(range(t * W, min((t + 1) * W, K))) for t in range(-(-K // W))]
+    if layout == "round-robin":
+        return [[k for t in range(s, len(tiles), S) for k in tiles[t]] for s in range(S)]
+    tps = -(-len(tiles) // S) if tiles else 0
+    return [[k for t in tiles[s * tps:(s + 1) * tps] for k in t] for s in range(S)]
+
+
+def combine(parts, scheme):
+    """serial: ((p0 + p1) + p2) + ...; pairwise: p_0 after the stride-halving
+    tree over the next power of two >= S (for S = 3: (p0 + p2) + p1)."""
+    if scheme == "serial":
+        acc = parts[0]
+        for p in parts[1:]:
+            acc = round_nearest_even(acc + p)
+        return acc
+    S = len(parts)
+    P = 1
+    while P < S:
+        P *= 2
+
+    def value(i, h):  # p_i after the levels with stride >= h
+        if h == P:
+            return parts[i]
+        left = value(i, 2 * h)
+        if i + h < S:
+            return round_nearest_even(left + value(i + h, 2 * h))
+        return left
+
+    return value(0, 1)
 
 
 # ---------------------------------------------------------------------------
@@ -260,33 +290,28 @@ def special(xrow, xfmt, wrow, wfmt, K):
     return None
 
 
-def accumulator(xrow, xfmt, wrow, wfmt, K, fast=True, S=1, B=32, F=13, Q=128, W=128):
+def accumulator(xrow, xfmt, wrow, wfmt, K, fast=True, S=1, B=32, F=13, Q=128, W=128,
+                layout="contiguous", scheme="serial"):
     """Accumulator of one output as a Fraction (F may be None only with fast
     accumulation and S = 1), or a special string."""
     sp = special(xrow, xfmt, wrow, wfmt, K)
     if sp is not None:
         return sp
-    nt = -(-K // W)
-    tps = -(-nt // S) if nt else 0
     parts = []
-    for s in range(S):
-        k0, k1 = min(s * tps * W, K), min((s + 1) * tps * W, K)
-        if k0 >= k1:
+    for ks in split_indices(K, S, W, layout):
+        if not ks:
             parts.append(Fraction(0))
         elif fast:
-            parts.append(chain(xrow, xfmt, wrow, wfmt, k0, k1, B, F))
+            parts.append(chain(xrow, xfmt, wrow, wfmt, 0, 0, B, F, ks=ks))
         else:
             a = Fraction(0)
-            for ck in range(k0, k1, Q):
-                a = round_nearest_even(a + chain(xrow, xfmt, wrow, wfmt, ck, min(ck + Q, k1), B, F))
+            for i in range(0, len(ks), Q):
+                a = round_nearest_even(a + chain(xrow, xfmt, wrow, wfmt, 0, 0, B, F, ks=ks[i:i + Q]))
             parts.append(a)
     if F is None:
         assert fast and S == 1, "unbounded bits only for one fast chain"
         return parts[0]
-    acc = parts[0]
-    for p in parts[1:]:
-        acc = round_nearest_even(acc + p)
-    return acc
+    return combine(parts, scheme)
 
 
 def accumulator_bits(*args, **kw) -> int:
@@ -300,7 +325,8 @@ def accumulator_bits(*args, **kw) -> int:
     return f32_bits_of(a)
 
 
-def scaled_mm(x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1, B=32, F=13, Q=128, W=128):
+def scaled_mm(x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1, B=32, F=13, Q=128, W=128,
+              layout="contiguous", scheme="serial"):
     """Tiny whole-matrix evaluation: returns (acc bits, output bits) as lists of lists."""
     M, K = len(x), (len(x[0]) if len(x) else 0)
     N = len(w)
@@ -308,7 +334,7 @@ def scaled_mm(x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1, B=
     for m in range(M):
         ra, ry = [], []
         for n in range(N):
-            a = accumulator_bits(x[m], xfmt, w[n], wfmt, K, fast, S, B, F, Q, W)
+            a = accumulator_bits(x[m], xfmt, w[n], wfmt, K, fast, S, B, F, Q, W, layout, scheme)
             ra.append(a)
             ry.append(epilogue_bits(a, sx_bits, sw_bits, out))
         accs.append(ra)

@@ -99,7 +99,8 @@ def pin_golden(o):
         sx = int(c.get("scale_x", "0x3F800000"), 16)
         sw = int(c.get("scale_w", "0x3F800000"), 16)
         out = c.get("out", "fp32")
-        acc, y = o.scaled_mm(x, c["xfmt"], w, c["wfmt"], sx, sw, out, c["fast"], c["S"])
+        acc, y = o.scaled_mm(x, c["xfmt"], w, c["wfmt"], sx, sw, out, c["fast"], c["S"],
+                             profile=c.get("profile", "hopper"))
         assert int(acc[0, 0]) == int(c["acc"], 16), (c["id"], hex(int(acc[0, 0])), c["acc"])
         if "y" in c:
             assert int(y[0, 0]) == int(c["y"], 16), (c["id"], hex(int(y[0, 0])), c["y"])
@@ -285,39 +286,54 @@ def pin_power_of_two_scaling(o, trials=30, seed=13):
 
 def pin_block_permutation(o, trials=30, seed=17):
     """The block step is symmetric in its products: permuting k inside each
-    aligned 32-block (x and w alike) changes nothing."""
+    aligned block (32 for hopper, 16 for the ada profiles; x and w alike)
+    changes nothing, for any split count."""
     rng = np.random.default_rng(seed)
     gen = torch.Generator().manual_seed(seed)
     for t in range(trials):
+        profile, B = (("hopper", 32), ("ada-serial", 16), ("ada-pairwise", 16))[t % 3]
         K = int(rng.integers(1, 20)) * 32
         x = _random_finite(rng, gen, (2, K), "e4m3fn")
         w = _random_finite(rng, gen, (3, K), "e4m3fn")
-        perm = np.concatenate([b * 32 + rng.permutation(32) for b in range(K // 32)])
-        fast, S = bool(t % 2), int(rng.integers(1, 3))
-        a1, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, S)
+        perm = np.concatenate([b * B + rng.permutation(B) for b in range(K // B)])
+        fast, S = bool(t % 2), int(rng.integers(1, 4))
+        a1, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, S,
+                            profile=profile)
         a2, _ = o.scaled_mm(x[:, perm], "e4m3fn", w[:, perm], "e4m3fn", 0x3F800000, 0x3F800000,
-                            "fp32", fast, S)
-        assert np.array_equal(a1, a2), (t, _first_diff(a1, a2))
+                            "fp32", fast, S, profile=profile)
+        assert np.array_equal(a1, a2), (t, profile, _first_diff(a1, a2))
 
 
 def pin_split_invariants(o, trials=20, seed=19):
     """S = 1 is the unsplit chain; with more splits than k-tiles the extra
-    splits are empty, so every S >= nt gives the same result as S = nt."""
+    splits are empty (+0, a no-op in either combination), so every S >= nt
+    gives the result of S = nt.  For the round-robin layout with S = 1 the
+    single split is the whole of K in order, the same as one contiguous
+    range with the same block width."""
     rng = np.random.default_rng(seed)
     gen = torch.Generator().manual_seed(seed)
     for t in range(trials):
         K = int(rng.integers(1, 20)) * 16
-        nt = -(-K // 128)
         x = _random_finite(rng, gen, (2, K), "e4m3fn")
         w = _random_finite(rng, gen, (2, K), "e4m3fn")
         fast = bool(t % 2)
-        ref, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, nt)
-        for S in (nt + 1, nt + 5):
-            a, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, S)
-            assert np.array_equal(a, ref), (t, S)
-        if nt == 1:
-            one, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, 1)
-            assert np.array_equal(one, ref)
+        for profile, W in (("hopper", 128), ("ada-serial", 64), ("ada-pairwise", 64)):
+            nt = -(-K // W)
+            ref, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, nt,
+                                 profile=profile)
+            for S in (nt + 1, nt + 5):
+                a, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, S,
+                                   profile=profile)
+                assert np.array_equal(a, ref), (t, profile, S)
+            if nt == 1:
+                one, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, 1,
+                                     profile=profile)
+                assert np.array_equal(one, ref)
+        rr, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, 1,
+                            profile="ada-serial")
+        flat, _ = o.scaled_mm(x, "e4m3fn", w, "e4m3fn", 0x3F800000, 0x3F800000, "fp32", fast, 1,
+                              profile=dict(B=16, W=K))
+        assert np.array_equal(rr, flat), t
 
 
 def pin_epilogue_random(o, n=20000, seed=23):
@@ -368,8 +384,9 @@ def pin_epilogue_random(o, n=20000, seed=23):
 
 def pin_spec_cross_check(o, trials=1500, seed=29):
     """The C oracle equals the independent Fraction formulation on random tiny
-    problems over both formats, all modes, several block widths and retained
-    bits, NaN and Inf codes, and non-power-of-two scales."""
+    problems over both formats, all modes, several block widths, retained
+    bits, split layouts and combinations, NaN and Inf codes, and
+    non-power-of-two scales."""
     rng = np.random.default_rng(seed)
     pyr = random.Random(seed)
     for t in range(trials):
@@ -384,15 +401,20 @@ def pin_spec_cross_check(o, trials=1500, seed=29):
         if t % 3 == 0:
             x[rng.random((M, K)) < 0.3] = 0
         fast = bool(t % 2)
-        S = int(rng.integers(1, 5))
-        B = pyr.choice([32, 32, 32, 16, 1, 5])
+        S = int(rng.integers(1, 6))
+        B = pyr.choice([32, 32, 32, 16, 16, 1, 5])
         F = pyr.choice([13, 13, 13, 4, 9, 20])
+        W = pyr.choice([128, 64, 64, 16, 48])
+        layout = pyr.choice(["contiguous", "round-robin"])
+        scheme = pyr.choice(["serial", "pairwise"])
         sx = int(bits32(np.float32(pyr.choice([1 / 64, 0.1, -3.0, 1e-30, 1 / 3]))))
         sw = int(bits32(np.float32(pyr.choice([1 / 32, 1 / 3, 7.0, 2.0 ** -120]))))
         out = pyr.choice(["bf16", "fp16", "fp32"])
-        acc, y = o.scaled_mm(x, xf, w, wf, sx, sw, out, fast, S, dict(B=B, F=F))
-        acc2, y2 = spec.scaled_mm(x.tolist(), xf, w.tolist(), wf, sx, sw, out, fast, S, B, F)
-        assert acc.tolist() == acc2 and y.tolist() == y2, (t, xf, wf, K, fast, S, B, F, out)
+        acc, y = o.scaled_mm(x, xf, w, wf, sx, sw, out, fast, S,
+                             dict(B=B, F=F, W=W, layout=layout, combine=scheme))
+        acc2, y2 = spec.scaled_mm(x.tolist(), xf, w.tolist(), wf, sx, sw, out, fast, S, B, F, 128, W,
+                                  layout, scheme)
+        assert acc.tolist() == acc2 and y.tolist() == y2, (t, xf, wf, K, fast, S, B, F, W, layout, scheme, out)
 
 
 # The quick suite the mutation tests run on every mutant.

@@ -28,6 +28,9 @@ MUTANTS = {
     15: "balanced instead of ceil-contiguous split layout",
     16: "non-canonical NaN pattern",
     17: "weight read transposed",
+    18: "round-robin split layout taken as contiguous runs",
+    19: "pairwise combination over adjacent pairs",
+    20: "round-robin k-tiles twice as wide",
 }
 
 
