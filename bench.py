@@ -43,6 +43,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the library's kernel sources (csrc/, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_exact_fp8_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     one exists for this workload and the current kernel source."""
@@ -52,9 +64,7 @@ def load_traffic(workload: str):
     try:
         with open(path) as f:
             d = json.load(f)
-        src = os.path.join(ROOT, "bit_exact_fp8_amd", "csrc", "emu_kernels.hip")
-        import hashlib
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_source_digest()
         if d.get("kernel_source_sha256") != digest:
             return None
         return d.get("hbm_bytes_per_launch")
@@ -62,7 +72,7 @@ def load_traffic(workload: str):
         return None
 
 
-def cpu_baseline(wl, x, w, y_gpu, budget_s: float):
+def cpu_baseline(wl, x, w, y_gpu, budget_s: float, profile: str = "hopper"):
     """Time the oracle on whole output rows, sized to about budget_s seconds."""
     import oracle
     orc = oracle.default()
@@ -74,7 +84,7 @@ def cpu_baseline(wl, x, w, y_gpu, budget_s: float):
     cols_probe = min(wl.N, 256)
     t0 = time.perf_counter()
     orc.scaled_mm(xs[:rows_probe], wl.xfmt, ws[:cols_probe], wl.wfmt, sx, sw, wl.out, wl.fast, wl.split_S,
-                  threads=threads)
+                  profile=profile, threads=threads)
     dt = max(time.perf_counter() - t0, 1e-3)
     rate = rows_probe * cols_probe * wl.K / dt  # MAC/s
     rows = int(max(threads, min(wl.M, budget_s * rate / (wl.N * wl.K))))
@@ -82,7 +92,7 @@ def cpu_baseline(wl, x, w, y_gpu, budget_s: float):
     rows = min(rows, wl.M)
     t0 = time.perf_counter()
     acc, y = orc.scaled_mm(xs[:rows], wl.xfmt, ws, wl.wfmt, sx, sw, wl.out, wl.fast, wl.split_S,
-                           threads=threads)
+                           profile=profile, threads=threads)
     dt = time.perf_counter() - t0
     ops = 2 * rows * wl.N * wl.K
     same = bool(np.array_equal(y, y_gpu[:rows]))
@@ -124,6 +134,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile configuration (tuning)")
+    ap.add_argument("--profile", default="hopper", choices=sorted(api.PROFILE),
+                    help="arithmetic profile (hopper is the pages' default)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -149,7 +161,7 @@ def main():
     sxd = torch.tensor([wl.scale_x], dtype=torch.float32, device=dev)
     swd = torch.tensor([wl.scale_w], dtype=torch.float32, device=dev)
     out = torch.empty((wl.M, wl.N), dtype=OUT_DTYPES[wl.out], device=dev)
-    ws_bytes = api.workspace_bytes(wl.M, wl.N, wl.K, wl.split_S, wl.fast)
+    ws_bytes = api.workspace_bytes(wl.M, wl.N, wl.K, wl.split_S, wl.fast, args.profile)
     wsbuf = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     lib = api._lib()
     if args.tile >= 0:
@@ -157,7 +169,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     call_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
                  wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), out.data_ptr(), api.OUT_DTYPE[out.dtype],
-                 wl.N, int(wl.fast), wl.split_S, 0, wsbuf.data_ptr(), ws_bytes, stream.cuda_stream)
+                 wl.N, int(wl.fast), wl.split_S, api.PROFILE[args.profile], wsbuf.data_ptr(), ws_bytes,
+                 stream.cuda_stream)
 
     def step():
         st = lib.emu_scaled_mm(*call_args)
@@ -200,7 +213,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {**wl.describe(), "parallelism": "single GPU"},
+        "config": {**wl.describe(), "profile": args.profile, "parallelism": "single GPU"},
         "roofline": {
             "bound": "alu",
             "achieved": achieved / 1e12,
@@ -214,7 +227,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, x, w, output_bits(out), args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, x, w, output_bits(out), args.cpu_budget, args.profile)
     print(json.dumps(result), flush=True)
 
 

@@ -23,7 +23,7 @@ EMU_OK, EMU_ERR_INVALID_ARG, EMU_ERR_REJECTED, EMU_ERR_UNSUPPORTED, EMU_ERR_WORK
 FP8_FORMAT = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
 FP8_FORMAT_NAME = {"e4m3fn": 0, "e5m2": 1}
 OUT_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
-PROFILE = {"hopper": 0}
+PROFILE = {"hopper": 0, "ada-serial": 1, "ada-pairwise": 2}
 
 
 class EmuError(RuntimeError):

@@ -1,19 +1,24 @@
-"""Build libemu_fp8gemm.so for gfx950 with hipcc (in-tree, next to this file)."""
+"""Build libemu_fp8gemm.so for gfx950 with hipcc (in-tree, next to this file).
+
+The main kernel's variants (block width x format pair) are separate
+translation units of emu_variant.hip, compiled in parallel and linked with
+the dispatcher, the combine kernel and the C ABI."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "emu_kernels.hip"), os.path.join(CSRC, "emu_api.cpp")]
 OUTPUT = os.path.join(PKG, "libemu_fp8gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-fno-fast-math", "-ffp-contract=off",
     # hipcc -O3 may form packed binary32 instructions on its own; keep them out
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -21,16 +26,37 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
+# (block width, x format, w format): e5m2 x e5m2 is rejected by the ABI.
+VARIANTS = [(b, xf, wf) for b in (32, 16) for xf, wf in ((0, 0), (0, 1), (1, 0))]
 
-def build(output: str = OUTPUT, extra_flags=None, verbose: bool = False) -> str:
-    tmp = output + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *SOURCES, "-o", tmp]
+
+def _units(objdir: str):
+    units = [(os.path.join(CSRC, "emu_kernels.hip"), os.path.join(objdir, "emu_kernels.o"), []),
+             (os.path.join(CSRC, "emu_api.cpp"), os.path.join(objdir, "emu_api.o"), [])]
+    for b, xf, wf in VARIANTS:
+        units.append((os.path.join(CSRC, "emu_variant.hip"), os.path.join(objdir, f"emu_variant_{b}_{xf}{wf}.o"),
+                      [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]))
+    return units
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
+        sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
         raise RuntimeError("hipcc failed to build libemu_fp8gemm.so")
+
+
+def build(output: str = OUTPUT, extra_flags=None, verbose: bool = False, jobs: int | None = None) -> str:
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="emu_build_") as objdir:
+        units = _units(objdir)
+        cmds = [[HIPCC, *FLAGS, *(extra_flags or []), *defs, "-c", src, "-o", obj] for src, obj, defs in units]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = output + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[obj for _, obj, _ in units], "-o", tmp], verbose)
     os.replace(tmp, output)
     return output
 

@@ -20,8 +20,15 @@ struct MainParams {
     int64_t ldx, ldw;
     int M, N;              // rows of this launch (M may be a slice)
     int64_t K;
-    int64_t split_len;     // K-length of every split, a multiple of 128 (>= K when unsplit)
-    int fast;              // 1: one chain per split; 0: restart every 128
+    // Split layout: K is cut into k-tiles of width 2^tile_shift.  Contiguous
+    // (round_robin = 0): split z owns tiles [z*tps, (z+1)*tps).  Round-robin:
+    // split z owns tiles z, z+S, z+2S, ...  Each split's chain (and slow
+    // chunking) runs along its tiles in increasing order.
+    int tile_shift;
+    int round_robin;
+    int64_t tps;
+    int S;
+    int fast;              // 1: one chain per split; 0: restart every 128 along the split
     int out_kind;          // OutKind
     void *out;             // OUT_ACC_F32 / epilogue destination, [M, N] with row stride ldo elements
     int64_t ldo;
@@ -32,6 +39,7 @@ struct MainParams {
 struct CombineParams {
     const float *part;     // [S, M, N] partials, dense
     int S, M, N;
+    int pairwise;          // 0: serial p0 + p1 + ...; 1: stride-halving pairwise tree
     int out_kind;          // OUT_ACC_F32 or an epilogue kind
     void *out;
     int64_t ldo;
@@ -58,8 +66,15 @@ struct TileShape {
 };
 TileShape tile_shape(int cfg);
 
-// Enqueue one main-kernel launch over grid (ceil(N/bn), ceil(M/bm), S).
-hipError_t launch_main(int cfg, int xfmt, int wfmt, const MainParams &p, int S, hipStream_t stream);
+// Enqueue one main-kernel launch over grid (ceil(N/bn), ceil(M/bm), S) with
+// blocks of `block` products (32 or 16).
+hipError_t launch_main(int cfg, int block, int xfmt, int wfmt, const MainParams &p, int S, hipStream_t stream);
+
+// One instantiation of the main kernel (block width BLK, x / w formats XF, WF:
+// 0 = e4m3fn, 1 = e5m2), defined in emu_main_kernel.h and instantiated by
+// emu_variant.hip.
+template <int BLK, int XF, int WF>
+hipError_t launch_variant(int cfg, const MainParams &p, int S, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 
 }  // namespace emu

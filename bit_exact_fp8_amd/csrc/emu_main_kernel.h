@@ -1,0 +1,868 @@
+// emu_main_kernel.h -- the main kernel of the bit-exact emulated FP8 GEMM
+// (gfx950), as templates; emu_variant.hip instantiates one block width and
+// format pair per translation unit.
+//
+// The arithmetic (mmaemu v0.1 pages: user guide section 1; validation page,
+// scope table rows "Hopper preset", "Ada instruction model", "Slow
+// accumulation", "Split-K", "Split-K on the H100 PCIe", "Epilogue", claims
+// tables; limitations page, corrections table): products are added in blocks
+// of 32 (hopper) or 16 (RTX 4060 profiles) along each split's k-list; each
+// block and the incoming accumulator c are aligned to the block's largest
+// exponent E (field exponents, subnormals at emin, zero products excluded);
+// every term and c are cut toward zero to the quantum 2^(E-13); the exact sum
+// is cut toward zero to 14 significant bits and becomes the new c (+0 when
+// zero).
+//
+// How one block is computed here, per output (m, n):
+//
+//  pass 1  E from packed 16-bit exponent planes: g = ea + eb with one
+//          v_pk_add_u16 per two products; the planes are biased so that
+//          every sum is a positive normal binary16 pattern, whose order is
+//          the integer order, and one v_pk_maximum3_f16 folds two pairs
+//          into the running maximum.  (Or on the matrix cores, see the power
+//          planes below.)
+//  pass 2  with C = 1.5 * 2^(E-13+23), a binary32 fma in round-toward-zero
+//          mode, fma(|a|, |b|, C), returns exactly C + trunc(|a*b| / 2^(E-13))
+//          * 2^(E-13): the product is exact inside the fma, C pins the
+//          result's binade to [2^(E+10), 2^(E+11)) whose ulp is the quantum,
+//          and round-toward-zero is the truncation.  The truncated magnitude
+//          (< 2^15) sits in the low 16 bits.  v_perm_b32 packs two of them,
+//          the sign pair (+-1, +-1) comes from one v_bitop3_b32 on packed
+//          sign masks, and v_dot2_i32_i16 applies the signs and accumulates.
+//  c       the same fma turns c into its truncated magnitude.
+//  block   T = signed sum (< 2^21, exact in an int); binary32(T) is exact and
+//          clearing its 10 low mantissa bits cuts it toward zero to 14
+//          significant bits; a multiplication by 2^(E-13), whose bits come
+//          from C's, gives the new c (exact).
+//
+// Round-toward-zero is set once per wave at kernel entry.  Every floating
+// point instruction whose rounding matters is written as inline assembly
+// that takes a token produced by the mode switch, so the compiler can neither
+// hoist it above the switch nor mix it with code that expects another mode.
+// The only round-to-nearest steps in this kernel, the slow-accumulation chunk
+// adds, switch the mode around themselves the same way.  All other floating
+// point operations here are exact (FP8 and small-integer conversions,
+// products of powers of two).  The epilogue rounds in integer arithmetic
+// (fp_round.h).
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "emu_internal.h"
+#include "fp_round.h"
+
+namespace emu {
+
+namespace {
+
+constexpr int FMT_E4M3 = 0;
+constexpr int FMT_E5M2 = 1;
+
+constexpr int KB = 32;           // k per LDS stage (one 32-product block or two 16-product blocks)
+constexpr int KP = KB / 2;       // packed pairs per stage
+constexpr int CHUNK = 128;       // slow-accumulation restart
+constexpr int A_STRIDE = KB + 4; // floats per LDS row of the value plane (16 B pad)
+constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent / sign planes
+
+// Exponent planes (one u16 per code).  A nonzero code stores
+// ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
+// bias 64 for x, 63 for w, so that a product's plane sum is
+// (g + 127) + 0x400: a positive normal binary16 pattern (the block maximum
+// can use binary16 maximum instructions, whose order on such patterns is the
+// integer order) whose low 9 bits are g + 127, directly comparable with the
+// binary32 exponent field of c.  A zero code stores ZERO_PLANE = 0x208: a
+// zero product's sum is then at most 0x208 + 0x200 + 79 = 0x400 + 87, below
+// every real product (g >= -20, i.e. 0x400 + 107) and every nonzero c
+// (|c| >= 2^-33, i.e. 0x400 + 94), and at least 0x400 + 16, which keeps the
+// quantum 2^(E-13) a normal binary32 value.
+constexpr uint32_t X_EBIAS = 64;
+constexpr uint32_t W_EBIAS = 63;
+constexpr uint32_t ZERO_PLANE = 0x208u;
+constexpr uint32_t SUM_OFFSET = 0x400u;
+// C = 1.5 * 2^(E + 10) has exponent field (E + 127) + 10 and fraction 0x400000.
+// (M << 23) drops M's bit 9 and above, so the 0x400 offset of the maximum
+// vanishes from C.
+constexpr uint32_t C_OFFSET = (10u << 23) | 0x400000u;
+// 2^q with q = E - 13 has exponent field (E + 127) - 13 = C's field - 23.
+constexpr uint32_t POW2Q_FROM_C = (23u << 23) | 0x400000u;
+
+// Exponent maximum on the matrix cores.  x codes become 2^(4*ex + 5), w codes
+// 2^(4*ew + 4), zeros 0 (bf16 "power planes").  For one quarter-block (8
+// consecutive k), sum_k of the products is S = sum of 2^(4*g_k + 9) over
+// the nonzero products: each term is exact in fp32 and
+// 2^(4G+9) <= S <= 8 * 2^(4G+9) = 2^(4G+12) for G = max g_k, so the binary32
+// exponent field of S, 4G + 136 .. 4G + 139, shifted right by 2 is exactly
+// G + 34.  This holds for any accumulation order and any faithful rounding
+// (the largest term is exact, adding nonnegative terms never goes below it
+// and 8 terms cannot reach 2^(4G+13)), so the matrix instruction's own
+// rounding cannot change the result.  A quarter with no nonzero product
+// gives S = 0, i.e. 0 after the shift, below every real product
+// (G >= -20 -> 14).  The biased block maximum is then
+// E + 127 = max over the four quarters of (S >> 25) + 93, compared with c's
+// binary32 exponent field (|c| >= 2^-33 -> 94 or more, c = 0 -> 0).
+constexpr uint32_t X_POW_OFF = 5;
+constexpr uint32_t W_POW_OFF = 4;
+constexpr uint32_t POW_TO_EB = 93;
+constexpr int PW_ROW = 8;  // words per (quarter, row) of a power plane: 8 real + 8 zero bf16
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_add_u16(uint32_t a, uint32_t b)
+{
+    us2 r = __builtin_bit_cast(us2, a) + __builtin_bit_cast(us2, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    us2 r = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// max(a, b, c) per 16-bit half, on positive normal binary16 patterns
+__device__ __forceinline__ uint32_t pk_max3_h(uint32_t a, uint32_t b, uint32_t c)
+{
+    h2 r = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b)), __builtin_bit_cast(h2, c));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// min(a, 1) per 16-bit half (written out: the compiler would unpack it)
+__device__ __forceinline__ uint32_t pk_min1_u16(uint32_t a)
+{
+    uint32_t r;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "s"(0x00010001u));
+    return r;
+}
+
+// max(lo16(g), hi16(g), lo16(e)), valid in the low 16 bits
+__device__ __forceinline__ uint32_t max3_lo_hi_u16(uint32_t g, uint32_t e)
+{
+    uint32_t r;
+    asm("v_max3_u16 %0, %1, %1, %2 op_sel:[0,1,0,0]" : "=v"(r) : "v"(g), "v"(e));
+    return r;
+}
+
+// (a.lo * b.lo + a.hi * b.hi) as signed 16-bit products, from zero
+__device__ __forceinline__ int dot2_i16_from0(uint32_t a, uint32_t b)
+{
+    int r;
+    asm("v_dot2_i32_i16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c)
+{
+    us2 r = __builtin_bit_cast(us2, a) * __builtin_bit_cast(us2, b) + __builtin_bit_cast(us2, c);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
+{
+    us2 r = __builtin_bit_cast(us2, a) * __builtin_bit_cast(us2, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, uint32_t sh)
+{
+    us2 r = __builtin_bit_cast(us2, a) >> (us2){(unsigned short)sh, (unsigned short)sh};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ int dot2_i16(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b), c, false);
+}
+
+// Exchange with the partner lane inside each quad: lane ^ 1 (quad_perm
+// [1,0,3,2]) and lane ^ 2 (quad_perm [2,3,0,1]).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+
+// ---- floating-point mode control -----------------------------------------
+// MODE register bits [1:0]: binary32 rounding (0 nearest even, 3 toward zero).
+__device__ __forceinline__ uint32_t mode_round_toward_zero()
+{
+    uint32_t tok;
+    asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\t"
+                 "s_nop 1\n\t"
+                 "s_mov_b32 %0, 0"
+                 : "=s"(tok)::"memory");
+    return tok;
+}
+
+// Switch to round-to-nearest-even once `dep` (a value computed in the current
+// mode) exists; returns a token for instructions that need the new mode.
+__device__ __forceinline__ uint32_t mode_round_nearest_after(uint32_t dep)
+{
+    uint32_t tok;
+    asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+                 "s_nop 1\n\t"
+                 "s_mov_b32 %0, 0"
+                 : "=s"(tok)
+                 : "v"(dep)
+                 : "memory");
+    return tok;
+}
+
+__device__ __forceinline__ uint32_t mode_round_toward_zero_after(uint32_t dep)
+{
+    uint32_t tok;
+    asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\t"
+                 "s_nop 1\n\t"
+                 "s_mov_b32 %0, 0"
+                 : "=s"(tok)
+                 : "v"(dep)
+                 : "memory");
+    return tok;
+}
+
+// fma(|a|, |b|, c) in the current (round-toward-zero) mode, as raw bits.
+__device__ __forceinline__ uint32_t fma_abs_rz(float a, float b, uint32_t c, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_fma_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "s"(tok));
+    return r;
+}
+
+// a * b where the product is exact (a power of two times a value of at most
+// 14 significant bits, in the normal range), in any mode.
+__device__ __forceinline__ uint32_t mul_exact(uint32_t a, uint32_t b, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b), "s"(tok));
+    return r;
+}
+
+// a + b in the current (round-to-nearest-even) mode.
+__device__ __forceinline__ uint32_t add_rn(uint32_t a, uint32_t b, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_add_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b), "s"(tok));
+    return r;
+}
+
+// ---- FP8 decoding -----------------------------------------------------------
+// Four codes of a row (one 32-bit word, k ascending from the low byte) become
+//   four signed binary32 values (exact hardware conversions, subnormals
+//   included),
+//   two exponent-plane pairs (u16 per code, see the plane constants above;
+//   subnormals take the field exponent emin, validation page claims table),
+//   two sign-mask pairs (u16 per code, 0xFFFF for a negative code, else 0).
+// NaN / Inf codes decode to something finite or not; outputs they touch are
+// overwritten by the specials rule, so their lanes' values do not matter.
+template <int FMT>
+__device__ __forceinline__ void cvt4(uint32_t w, float &v0, float &v1, float &v2, float &v3)
+{
+    if (FMT == FMT_E4M3) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+        v0 = lo[0]; v1 = lo[1]; v2 = hi[0]; v3 = hi[1];
+    } else {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+        v0 = lo[0]; v1 = lo[1]; v2 = hi[0]; v3 = hi[1];
+    }
+}
+
+// Exponent-plane pair of two codes held as [code0, 0, code1, 0].
+template <int FMT, uint32_t EBIAS>
+__device__ __forceinline__ uint32_t plane_pair(uint32_t p)
+{
+    constexpr uint32_t FBIAS = (FMT == FMT_E4M3) ? 7u : 15u;
+    constexpr uint32_t SH = (FMT == FMT_E4M3) ? 3u : 2u;
+    // nonzero: max(ef, 1) - FBIAS + 0x200 + EBIAS = (max(ef,1) + K) * 1 + ZERO_PLANE
+    constexpr uint32_t K = 0x200u + EBIAS - FBIAS - ZERO_PLANE;
+    const uint32_t mag = p & 0x007F007Fu;
+    const uint32_t ef = pk_shr_u16(mag, SH);
+    const uint32_t nz = pk_min1_u16(mag);
+    const uint32_t pl = pk_add_u16(__builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                                       __builtin_bit_cast(us2, ef), (us2){1, 1})),
+                                   K | (K << 16));
+    return pk_mad_u16(pl, nz, ZERO_PLANE | (ZERO_PLANE << 16));
+}
+
+// Power-plane pair (bf16 bits of 2^(4*ex + OFF), 0 for a zero code) of two
+// codes held as [code0, 0, code1, 0]; ex is the field exponent (emin for
+// subnormals).  bf16 bits of 2^E are (E + 127) << 7, and
+// E + 127 = 4*max(ef, 1) + (OFF + 127 - 4*FBIAS).
+template <int FMT, uint32_t OFF>
+__device__ __forceinline__ uint32_t power_pair(uint32_t p)
+{
+    constexpr uint32_t FBIAS = (FMT == FMT_E4M3) ? 7u : 15u;
+    constexpr uint32_t SH = (FMT == FMT_E4M3) ? 3u : 2u;
+    constexpr uint32_t K = (OFF + 127u - 4u * FBIAS) << 7;
+    const uint32_t mag = p & 0x007F007Fu;
+    const uint32_t ef = pk_shr_u16(mag, SH);
+    const uint32_t nz = pk_min1_u16(mag);
+    const uint32_t efc = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, ef), (us2){1, 1}));
+    return pk_mul_u16(pk_mad_u16(efc, 0x02000200u, K | (K << 16)), nz);
+}
+
+// Decode 16 consecutive codes of one row into the value and sign planes and
+// the power plane (the two quarter-blocks the 16 codes cover, 8 codes each).
+template <int FMT, uint32_t OFF>
+__device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *vs, uint32_t *pq0, uint32_t *pq1)
+{
+    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[16];
+    uint32_t pp[8], sp[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = words[q];
+        cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        pp[2 * q] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
+        pp[2 * q + 1] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+        const uint32_t t = w << 8;
+        sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
+        sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
+    *reinterpret_cast<uint4 *>(pq0) = make_uint4(pp[0], pp[1], pp[2], pp[3]);
+    *reinterpret_cast<uint4 *>(pq1) = make_uint4(pp[4], pp[5], pp[6], pp[7]);
+}
+
+// Decode 16 consecutive codes of one row into the LDS planes.
+template <int FMT, uint32_t EBIAS>
+__device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve, uint32_t *vs)
+{
+    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[16];
+    uint32_t ep[8], sp[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = words[q];
+        cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        ep[2 * q] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
+        ep[2 * q + 1] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+        // v_perm selectors 8..11 replicate the top bit of bytes 1, 3 of the
+        // second source and bytes 1, 3 of the first: with (w << 8, w) these
+        // are the signs of codes 1, 3, 0, 2.
+        const uint32_t t = w << 8;
+        sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
+        sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        *reinterpret_cast<uint4 *>(ve + 4 * q) = make_uint4(ep[4 * q], ep[4 * q + 1], ep[4 * q + 2], ep[4 * q + 3]);
+        *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
+    }
+}
+
+// Any NaN (E4M3) or Inf/NaN (E5M2) code among four packed codes.
+template <int FMT>
+__device__ __forceinline__ uint32_t has_special(uint32_t v)
+{
+    if (FMT == FMT_E4M3) return ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    return ((v & 0x7C7C7C7Cu) + 0x04040404u) & 0x80808080u;
+}
+
+template <int FMT>
+__device__ __forceinline__ void classify(uint32_t code, bool &nan, bool &inf, bool &zero, uint32_t &sign)
+{
+    sign = code >> 7;
+    if (FMT == FMT_E4M3) {
+        nan = (code & 0x7Fu) == 0x7Fu;
+        inf = false;
+        zero = (code & 0x7Fu) == 0;
+    } else {
+        nan = (code & 0x7Cu) == 0x7Cu && (code & 3u);
+        inf = (code & 0x7Fu) == 0x7Cu;
+        zero = (code & 0x7Fu) == 0;
+    }
+}
+
+// The k-list of one split: positions 0 .. len-1 along its k-tiles (width
+// 2^shift; tile `first`, then every `stride`-th), k = tile * W + offset.
+struct SplitSeq {
+    int64_t first, stride, len;
+    int shift;
+    __device__ __forceinline__ int64_t k_of(int64_t pos) const
+    {
+        return ((first + (pos >> shift) * stride) << shift) + (pos & ((int64_t(1) << shift) - 1));
+    }
+};
+
+__device__ __forceinline__ SplitSeq split_seq(const MainParams &p, int z)
+{
+    const int64_t W = int64_t(1) << p.tile_shift;
+    const int64_t nt = (p.K + W - 1) >> p.tile_shift;
+    SplitSeq q;
+    q.shift = p.tile_shift;
+    int64_t ntiles;
+    if (p.round_robin) {
+        q.first = z;
+        q.stride = p.S;
+        ntiles = (z < nt) ? (nt - z + p.S - 1) / p.S : 0;
+    } else {
+        q.first = (int64_t)z * p.tps;
+        q.stride = 1;
+        ntiles = (q.first < nt) ? ((p.tps < nt - q.first) ? p.tps : nt - q.first) : 0;
+    }
+    q.len = 0;
+    if (ntiles > 0) {
+        const int64_t last = q.first + (ntiles - 1) * q.stride;
+        const int64_t tail = p.K - (last << p.tile_shift);
+        q.len = ((ntiles - 1) << p.tile_shift) + (tail < W ? tail : W);
+    }
+    return q;
+}
+
+// The non-finite result of one output over a split's k-list: NaN if a NaN
+// code is in either row, if some k pairs an infinity with a zero, or if
+// infinite products of both signs occur; otherwise the signed infinity.
+// Only called for rows that hold a NaN or Inf code in that k-list, so the
+// result is never finite.
+template <int XF, int WF>
+__device__ uint32_t special_acc(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq)
+{
+    bool nan = false, pos = false, neg = false;
+    for (int64_t i = 0; i < sq.len; ++i) {
+        const int64_t k = sq.k_of(i);
+        bool an, ai, az, bn, bi, bz;
+        uint32_t as, bs;
+        classify<XF>(xr[k], an, ai, az, as);
+        classify<WF>(wr[k], bn, bi, bz, bs);
+        if (an || bn) nan = true;
+        else if (ai || bi) {
+            if (az || bz) nan = true;
+            else if (as ^ bs) neg = true;
+            else pos = true;
+        }
+    }
+    if (nan || (pos && neg)) return kCanonNan32;
+    return neg ? 0xFF800000u : 0x7F800000u;
+}
+
+__device__ __forceinline__ void store_output(const MainParams &p, int64_t m, int64_t n, uint32_t acc,
+                                             uint32_t alpha, int split)
+{
+    if (p.out_kind == OUT_ACC_F32) {
+        float *o = reinterpret_cast<float *>(p.out) + split * p.split_stride;
+        reinterpret_cast<uint32_t *>(o)[m * p.ldo + n] = canon_f32(acc);
+        return;
+    }
+    const uint32_t y = epilogue_f32(acc, alpha);
+    if (p.out_kind == OUT_BF16)
+        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_bf16(y);
+    else if (p.out_kind == OUT_F16)
+        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_f16(y);
+    else
+        reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(y);
+}
+
+// ---- the main kernel ---------------------------------------------------------
+// Workgroup tile BM x BN outputs of one split; thread tile RM x RN with rows
+// tm + i*TM and columns tn + j*TN (interleaved, so that the lanes of a wave
+// read consecutive, padded LDS rows).
+// Minimum waves per SIMD the register allocation must allow for a thread tile.
+template <int RM, int RN>
+struct WavesPerSimd {
+    static constexpr int value = (RM * RN >= 16) ? 2 : 4;
+};
+
+// G lanes share each output chain (G = 1, 2 or 4): lane g of a chain takes
+// the g-th of G equal slices of every block; the block maximum and the block
+// sum are combined across the G lanes with quad DPP moves, and every lane of
+// the chain then carries the same accumulator.
+//
+// BLK products per block (32: hopper; 16: the RTX 4060 profiles).  The LDS
+// stage is always 32 k wide; with BLK = 16 it holds two blocks, stepped in
+// order.
+//
+// MX: the block maximum comes from bf16 matrix instructions (see the power
+// planes above) instead of packed VALU maxima.  Needs RM = 4, G = 1 and one
+// wave per 16 rows: the wave's 16 x (16*RN) output tile is RN 16x16
+// matrix-instruction tiles, and lane l owns rows 4*(l/16) + i and columns
+// l%16 + 16*j, the layout of v_mfma_f32_16x16x16_bf16's result.
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST, bool MX, int BLK>
+__global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
+{
+    static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
+    static_assert(BLK == 32 || BLK == 16, "blocks of 32 or 16 products");
+    static_assert(!MX || (RM == 4 && G == 1 && BN == 16 * RN && (BM / 16) * 64 == (BM / RM) * (BN / RN)),
+                  "matrix-instruction exponents need 16-row waves with 4x RN thread tiles");
+    constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
+    constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per stage: two per row
+    constexpr int CPT = (NCHUNK + NT - 1) / NT;
+    constexpr int NBS = KB / BLK;          // blocks per stage
+    constexpr int QPB = BLK / 8;           // quarter-blocks (8 products) per block
+    constexpr int WPB = BLK / 2;           // exponent-plane words per block
+    constexpr int WPL = WPB / G;           // ... per lane
+    constexpr int WU = (WPL >= 4) ? 4 : 2; // words per exponent-plane read
+    constexpr int K4PL = BLK / 4 / G;      // groups of 4 products per lane and block
+    static_assert(WPL % WU == 0 && K4PL >= 1, "block slice per lane");
+
+    __shared__ __attribute__((aligned(16))) float xa[BM * A_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xe[MX ? 4 : BM * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xs[BM * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) float wa[BN * A_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t we[MX ? 4 : BN * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t wsg[BN * P_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
+    __shared__ uint32_t flags[BM + BN];
+
+    const int t = threadIdx.x;
+    const int lane_g = t % G, slot = t / G;
+    const int tn = slot % TN, tm = slot / TN;
+    const int wave = t >> 6, lane = t & 63;
+    // local row of chain i, local column of chain j
+    auto row_of = [&](int i) { return MX ? 16 * wave + 4 * (lane >> 4) + i : tm + i * TM; };
+    auto col_of = [&](int j) { return MX ? (lane & 15) + 16 * j : tn + j * TN; };
+
+    if (MX) {  // zero the power planes once: the upper 8 bf16 of every quarter row stay zero
+        for (int i = t; i < BM * PW_ROW; i += NT) reinterpret_cast<uint4 *>(xp)[i] = make_uint4(0, 0, 0, 0);
+        for (int i = t; i < BN * PW_ROW; i += NT) reinterpret_cast<uint4 *>(wp)[i] = make_uint4(0, 0, 0, 0);
+    }
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int split = blockIdx.z;
+    const SplitSeq sq = split_seq(p, split);
+    const int64_t tile_mask = (int64_t(1) << p.tile_shift) - 1;
+
+    for (int i = t; i < BM + BN; i += NT) flags[i] = 0;
+
+    // chunk q of this thread: row r = idx >> 1 (x rows first), half = idx & 1
+    uint32_t myflag[CPT];
+    uint4 raw[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) myflag[q] = 0;
+
+    // Stage at sequence position pos (a multiple of 32, inside one k-tile):
+    // k from sq.k_of(pos), up to the end of that tile or of K; codes past it
+    // load as zeros (zero products: neutral in every block).
+    auto load_block = [&](int64_t pos) {
+        const int64_t kb = sq.k_of(pos);
+        const int64_t tile_end = kb - (pos & tile_mask) + tile_mask + 1;
+        const int64_t lim = tile_end < p.K ? tile_end : p.K;
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int idx = t + q * NT;
+            raw[q] = make_uint4(0, 0, 0, 0);
+            if (idx < NCHUNK) {
+                const int r = idx >> 1, half = idx & 1;
+                const int64_t k = kb + 16 * half;
+                if (k < lim) {
+                    if (r < BM) {
+                        if (m0 + r < p.M) raw[q] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + k);
+                    } else if (n0 + (r - BM) < p.N) {
+                        raw[q] = *reinterpret_cast<const uint4 *>(p.w + (n0 + r - BM) * p.ldw + k);
+                    }
+                }
+            }
+        }
+    };
+
+    uint32_t tok = mode_round_toward_zero();
+
+    uint32_t c[RM][RN];
+    uint32_t slow[FAST ? 1 : RM][FAST ? 1 : RN];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) c[i][j] = 0u;
+    if (!FAST) {
+#pragma unroll
+        for (int i = 0; i < (FAST ? 1 : RM); ++i)
+#pragma unroll
+            for (int j = 0; j < (FAST ? 1 : RN); ++j) slow[i][j] = 0u;
+    }
+
+    if (sq.len > 0) load_block(0);
+    for (int64_t pos = 0; pos < sq.len; pos += KB) {
+        __syncthreads();  // previous stage's readers are done with the LDS planes
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int idx = t + q * NT;
+            if (idx < NCHUNK) {
+                const int r = idx >> 1, half = idx & 1;
+                if (r < BM) {
+                    myflag[q] |= has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
+                                 has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
+                    if (MX)
+                        decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
+                                                       xs + r * P_STRIDE + 8 * half,
+                                                       xp + ((2 * half) * BM + r) * PW_ROW,
+                                                       xp + ((2 * half + 1) * BM + r) * PW_ROW);
+                    else
+                        decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
+                                                  xe + r * P_STRIDE + 8 * half, xs + r * P_STRIDE + 8 * half);
+                } else {
+                    const int rw = r - BM;
+                    myflag[q] |= has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
+                                 has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
+                    if (MX)
+                        decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
+                                                       wsg + rw * P_STRIDE + 8 * half,
+                                                       wp + ((2 * half) * BN + rw) * PW_ROW,
+                                                       wp + ((2 * half + 1) * BN + rw) * PW_ROW);
+                    else
+                        decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
+                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * P_STRIDE + 8 * half);
+                }
+            }
+        }
+        __syncthreads();
+        if (pos + KB < sq.len) load_block(pos + KB);  // prefetch; latency hidden by the compute below
+
+#pragma unroll
+        for (int hb = 0; hb < NBS; ++hb) {
+            uint32_t Cb[RM][RN];
+            int acc[RM][RN];
+            if constexpr (MX) {
+                // pass 1 on the matrix cores: per quarter-block, S for every output
+                uint32_t smax[RM][RN];
+#pragma unroll
+                for (int qq = 0; qq < QPB; ++qq) {
+                    const int qb = hb * QPB + qq;
+                    const s4 a = *reinterpret_cast<const s4 *>(xp + (qb * BM + 16 * wave + (lane & 15)) * PW_ROW +
+                                                               2 * (lane >> 4));
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) {
+                        const s4 b = *reinterpret_cast<const s4 *>(wp + (qb * BN + 16 * j + (lane & 15)) * PW_ROW +
+                                                                   2 * (lane >> 4));
+                        const f4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < RM; ++i)
+                            smax[i][j] = qq ? max(smax[i][j], __float_as_uint(d[i])) : __float_as_uint(d[i]);
+                    }
+                }
+                // block prologue: C and the truncated incoming accumulator
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) {
+                        const uint32_t eb = max((smax[i][j] >> 25) + POW_TO_EB, (c[i][j] >> 23) & 0xFFu);
+                        Cb[i][j] = (eb << 23) + C_OFFSET;
+                        const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
+                        const uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                        acc[i][j] = dot2_i16_from0(rc, sc);
+                    }
+            } else {
+                // pass 1: E per output, from this lane's slice of the block
+                uint32_t gmax[RM][RN];
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) gmax[i][j] = 0u;
+#pragma unroll 1
+                for (int wo = hb * WPB + lane_g * WPL; wo < hb * WPB + (lane_g + 1) * WPL; wo += WU) {
+                    if constexpr (WU == 4) {
+                        uint4 ea[RM], eb[RN];
+#pragma unroll
+                        for (int i = 0; i < RM; ++i)
+                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * P_STRIDE + wo);
+#pragma unroll
+                        for (int j = 0; j < RN; ++j)
+                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * P_STRIDE + wo);
+#pragma unroll
+                        for (int i = 0; i < RM; ++i)
+#pragma unroll
+                            for (int j = 0; j < RN; ++j) {
+                                uint32_t g = gmax[i][j];
+                                g = pk_max3_h(g, pk_add_u16(ea[i].x, eb[j].x), pk_add_u16(ea[i].y, eb[j].y));
+                                g = pk_max3_h(g, pk_add_u16(ea[i].z, eb[j].z), pk_add_u16(ea[i].w, eb[j].w));
+                                gmax[i][j] = g;
+                            }
+                    } else {
+                        uint2 ea[RM], eb[RN];
+#pragma unroll
+                        for (int i = 0; i < RM; ++i)
+                            ea[i] = *reinterpret_cast<const uint2 *>(xe + (tm + i * TM) * P_STRIDE + wo);
+#pragma unroll
+                        for (int j = 0; j < RN; ++j)
+                            eb[j] = *reinterpret_cast<const uint2 *>(we + (tn + j * TN) * P_STRIDE + wo);
+#pragma unroll
+                        for (int i = 0; i < RM; ++i)
+#pragma unroll
+                            for (int j = 0; j < RN; ++j)
+                                gmax[i][j] = pk_max3_h(gmax[i][j], pk_add_u16(ea[i].x, eb[j].x),
+                                                       pk_add_u16(ea[i].y, eb[j].y));
+                    }
+                }
+
+                if (G >= 2) {
+#pragma unroll
+                    for (int i = 0; i < RM; ++i)
+#pragma unroll
+                        for (int j = 0; j < RN; ++j) {
+                            uint32_t g = gmax[i][j];
+                            if (G == 2) g = pk_max3_h(g, quad_xor1(g), g);
+                            if (G == 4) g = pk_max3_h(g, quad_xor1(g), quad_xor2(g));
+                            if (G == 4) g = pk_max3_h(g, quad_xor1(g), g);
+                            gmax[i][j] = g;
+                        }
+                }
+
+                // block prologue: C and the truncated incoming accumulator
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) {
+                        const uint32_t g = gmax[i][j];
+                        const uint32_t ec = ((c[i][j] >> 23) & 0xFFu) | SUM_OFFSET;
+                        // only the low 9 bits of the maximum reach C
+                        Cb[i][j] = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
+                        const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
+                        // (+-1, 0) applies c's sign to the truncated magnitude in the low half
+                        uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
+                        if (G > 1) sc = (lane_g == 0) ? sc : 0u;  // c enters the block sum once
+                        acc[i][j] = dot2_i16_from0(rc, sc);
+                    }
+            }
+
+            // pass 2: truncated terms, signs, accumulation
+#pragma unroll 1
+            for (int k4 = hb * (BLK / 4) + lane_g * K4PL; k4 < hb * (BLK / 4) + (lane_g + 1) * K4PL; ++k4) {
+                float4 av[RM], bv[RN];
+                uint2 sa[RM], sb[RN];
+#pragma unroll
+                for (int i = 0; i < RM; ++i) {
+                    av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
+                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * P_STRIDE + 2 * k4);
+                }
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
+                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * P_STRIDE + 2 * k4);
+                }
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) {
+                        const uint32_t C = Cb[i][j];
+                        const uint32_t r0 = fma_abs_rz(av[i].x, bv[j].x, C, tok);
+                        const uint32_t r1 = fma_abs_rz(av[i].y, bv[j].y, C, tok);
+                        const uint32_t r2 = fma_abs_rz(av[i].z, bv[j].z, C, tok);
+                        const uint32_t r3 = fma_abs_rz(av[i].w, bv[j].w, C, tok);
+                        int a = acc[i][j];
+                        a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), (sa[i].x ^ sb[j].x) | 0x00010001u, a);
+                        a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), (sa[i].y ^ sb[j].y) | 0x00010001u, a);
+                        acc[i][j] = a;
+                    }
+            }
+
+            if (G >= 2) {
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) {
+                        int a = acc[i][j];
+                        a += (int)quad_xor1((uint32_t)a);
+                        if (G == 4) a += (int)quad_xor2((uint32_t)a);
+                        acc[i][j] = a;
+                    }
+            }
+
+            // block epilogue: cut the exact sum to 14 significant bits, scale by 2^q
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    const uint32_t tb = __float_as_uint((float)acc[i][j]) & 0xFFFFFC00u;
+                    c[i][j] = mul_exact(tb, Cb[i][j] - POW2Q_FROM_C, tok);
+                }
+        }
+
+        // slow accumulation: add the chunk result every 128 positions of the
+        // split's k-list, in order
+        if (!FAST && (((pos + KB) & (CHUNK - 1)) == 0 || pos + KB >= sq.len)) {
+            uint32_t dep = 0;
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) dep |= c[i][j];
+            const uint32_t tok_rn = mode_round_nearest_after(dep);
+            uint32_t dep2 = 0;
+#pragma unroll
+            for (int i = 0; i < (FAST ? 1 : RM); ++i)
+#pragma unroll
+                for (int j = 0; j < (FAST ? 1 : RN); ++j) {
+                    slow[i][j] = add_rn(slow[i][j], c[i][j], tok_rn);
+                    dep2 |= slow[i][j];
+                    c[i][j] = 0u;
+                }
+            tok = mode_round_toward_zero_after(dep2);
+        }
+    }
+
+    // rows holding NaN / Inf codes in this split's k-list
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+        const int idx = t + q * NT;
+        if (idx < NCHUNK && myflag[q]) atomicOr(&flags[idx >> 1], 1u);
+    }
+    __syncthreads();
+
+    uint32_t alpha = 0;  // the scales are read only when the epilogue runs here
+    if (p.out_kind != OUT_ACC_F32) alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            const int rm = row_of(i), rn = col_of(j);
+            const int64_t m = m0 + rm, n = n0 + rn;
+            if (m >= p.M || n >= p.N || lane_g != 0) continue;
+            uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
+            if (flags[rm] | flags[BM + rn]) a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq);
+            store_output(p, m, n, a, alpha, split);
+        }
+}
+
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool MX, int BLK>
+hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
+{
+    constexpr int NT = (BM / RM) * (BN / RN) * G;
+    dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, S);
+    if (p.fast)
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true, MX, BLK>), grid, dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false, MX, BLK>), grid, dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int XF, int WF, int BLK>
+hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
+{
+    switch (cfg) {
+    case TILE_64x128: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, false, BLK>(p, S, stream);
+    case TILE_64x64: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, false, BLK>(p, S, stream);
+    case TILE_32x64: return launch_cfg<XF, WF, 32, 64, 2, 4, 1, false, BLK>(p, S, stream);
+    case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK>(p, S, stream);
+    case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2, false, BLK>(p, S, stream);
+    case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4, false, BLK>(p, S, stream);
+    case TILE_64x64_MX: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, S, stream);
+    case TILE_64x128_MX: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, S, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
+// All tile configurations of one block width and format pair.
+template <int BLK, int XF, int WF>
+hipError_t launch_variant(int cfg, const MainParams &p, int S, hipStream_t stream)
+{
+    return launch_fmt<XF, WF, BLK>(cfg, p, S, stream);
+}
+
+}  // namespace emu

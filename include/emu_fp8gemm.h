@@ -5,9 +5,11 @@
  * mmaemu v0.1 documentation describes for its default "hopper" profile
  * (user guide section 1 and section 3 "A first GEMM"; validation page,
  * scope table rows "Hopper preset", "Slow accumulation", "Split-K on the
- * H100 PCIe" and "Epilogue"; limitations page, corrections table):
+ * H100 PCIe" and "Epilogue"; limitations page, corrections table), and for
+ * its RTX 4060 profiles, which differ only in block width and split layout
+ * (see emu_profile below):
  *
- *  - E4M3/E5M2 products are added in blocks of 32 consecutive products; each
+ *  - E4M3/E5M2 products are added in blocks of 32 (hopper) consecutive products; each
  *    block, together with the incoming accumulator, is aligned to the block's
  *    largest exponent (field exponents, subnormals at emin), every term is cut
  *    toward zero to 13 fraction bits, and the block sum is cut toward zero to
@@ -67,7 +69,8 @@ typedef enum {
     EMU_ERR_REJECTED = 2,    /* a call torch 2.7.1 / cuBLASLt would reject (limitations page, features table):
                                 e5m2 x e5m2, K or N not a multiple of 16, x / w / out not 16-byte aligned,
                                 ldx or ldw not a multiple of 16 */
-    EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: FP8 outputs, profiles other than hopper */
+    EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: FP8 outputs, split_S above 65535,
+                                M or N above 2^31-1 */
     EMU_ERR_WORKSPACE = 4,   /* workspace_bytes < emu_workspace_bytes(...) */
     EMU_ERR_DEVICE = 5       /* a HIP launch or runtime error */
 } emu_status;
@@ -84,9 +87,28 @@ typedef enum {
     EMU_OUT_E5M2 = 4
 } emu_out_dtype;
 
-/* The arithmetic profile.  Only the default H100 PCIe profile "hopper" is
- * built (user guide section 4: hopper is the default). */
-typedef enum { EMU_PROFILE_HOPPER = 0 } emu_profile;
+/* The arithmetic profile (user guide section 4: profiles name a reference
+ * platform; hopper is the default).
+ *   EMU_PROFILE_HOPPER: the H100 PCIe -- 32-product blocks; split_S > 1 cuts
+ *     K into contiguous runs of 128-wide k-tiles (ceil layout), partials
+ *     added serially.
+ *   EMU_PROFILE_ADA_SERIAL / EMU_PROFILE_ADA_PAIRWISE: the RTX 4060 --
+ *     16-product blocks (validation page, scope table row "Ada instruction
+ *     model"); split_S > 1 deals 64-wide k-tiles round-robin to the splits
+ *     (tile t to split t mod S), each split chains (and, for slow
+ *     accumulation, restarts every 128) along its own tiles in order, and
+ *     the partials are added serially or by the pairwise tree (limitations
+ *     page, corrections table; validation page, claims table: for S = 3
+ *     pairwise is (p2 + p0) + p1).  The pairwise tree for other S is a
+ *     reading: p_i += p_{i+h} for h = P/2, P/4, ..., 1 (P the next power of
+ *     two >= S) wherever i + h < S; the result is p_0.
+ * The block step, the 13 retained fraction bits, c in the alignment, slow
+ * accumulation and the epilogue are the same for all profiles. */
+typedef enum {
+    EMU_PROFILE_HOPPER = 0,
+    EMU_PROFILE_ADA_SERIAL = 1,
+    EMU_PROFILE_ADA_PAIRWISE = 2
+} emu_profile;
 
 /*
  * y = (x @ w.T) * scale_x * scale_w (torch._scaled_mm semantics with

@@ -85,7 +85,7 @@ CASES = [
     (dict(ldx=40), api.EMU_ERR_REJECTED),
     (dict(od=3), api.EMU_ERR_UNSUPPORTED),       # FP8 outputs
     (dict(od=4), api.EMU_ERR_UNSUPPORTED),
-    (dict(prof=1), api.EMU_ERR_UNSUPPORTED),
+    (dict(prof=3), api.EMU_ERR_INVALID_ARG),     # unknown profile
     (dict(S=2), api.EMU_ERR_WORKSPACE),
     (dict(S=2, ws=16, wsb=100), api.EMU_ERR_WORKSPACE),
 ]
@@ -117,6 +117,24 @@ def test_page_parameters_match_the_library_split_rule():
     assert params["split_tile"]["value"] == 128 and "128-wide k-tiles" in hdr
     assert params["block_products"]["value"] == 32 and "blocks of 32" in hdr
     assert params["fraction_bits"]["value"] == 13 and "13 fraction bits" in hdr
+
+
+def test_page_parameters_match_the_ada_profiles():
+    """The RTX 4060 profiles the library documents use the pages' block width,
+    tile width, layout and combinations, and the oracle's profiles agree."""
+    import oracle
+    params = json.load(open(os.path.join(ROOT, "tests", "golden", "page_parameters.json")))["ada"]
+    hdr = open(os.path.join(ROOT, "include", "emu_fp8gemm.h")).read()
+    assert params["block_products"]["value"] == 16 and "16-product blocks" in hdr
+    assert params["split_tile"]["value"] == 64 and "64-wide k-tiles" in hdr
+    assert "round-robin" in hdr and "(p2 + p0) + p1" in hdr
+    for name, scheme in (("ada-serial", "serial"), ("ada-pairwise", "pairwise")):
+        pf = oracle.PROFILES[name]
+        assert pf["B"] == params["block_products"]["value"] and pf["W"] == params["split_tile"]["value"]
+        assert pf["F"] == params["fraction_bits"]["value"] and pf["Q"] == params["slow_chunk"]["value"]
+        assert pf["layout"] == params["split_layout"]["value"] and scheme in params["combine_order"]["value"]
+        assert pf["combine"] == scheme
+        assert api.PROFILE[name] in (1, 2)
 
 
 # ---- host builds of the kernels' rounding routines -------------------------

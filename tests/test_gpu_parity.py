@@ -47,7 +47,8 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
 
 
-def gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, stream=None, prefill=None):
+def gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, stream=None, prefill=None,
+            profile="hopper"):
     xd = x.to(dev).view(FP8_DTYPES[xfmt])
     wd = w.to(dev).view(FP8_DTYPES[wfmt])
     sxd = torch.tensor([sx], dtype=torch.float32, device=dev)
@@ -58,15 +59,15 @@ def gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, stream=No
         o.view(torch.uint8).fill_(prefill)
     with torch.cuda.stream(stream or torch.cuda.current_stream(dev)):
         y = api.scaled_mm(xd, wd.t(), sxd, swd, out_dtype=OUT_DTYPES[out], use_fast_accum=fast,
-                          split_S=S, out=o)
-        acc = api.accumulate(xd, wd, use_fast_accum=fast, split_S=S)
+                          split_S=S, profile=profile, out=o)
+        acc = api.accumulate(xd, wd, use_fast_accum=fast, split_S=S, profile=profile)
     torch.cuda.synchronize(dev)
     return bits_of(y), bits_of(acc)
 
 
-def oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1):
+def oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, profile="hopper"):
     return orc.scaled_mm(x.numpy(), xfmt, w.numpy(), wfmt, scale_bits(sx), scale_bits(sw), out, fast, S,
-                         threads=THREADS)
+                         profile=profile, threads=THREADS)
 
 
 def assert_same(got, want, what):
@@ -78,11 +79,11 @@ def assert_same(got, want, what):
                              f"gpu {int(got[i]):#x} oracle {int(want[i]):#x}")
 
 
-def check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, what):
+def check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, what, profile="hopper"):
     note(f"[gpu] {what}: M={x.shape[0]} N={w.shape[0]} K={x.shape[1]} {xfmt}x{wfmt} "
-         f"fast={fast} S={S} out={out}")
-    y, acc = gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out, fast, S)
-    acc_o, y_o = oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out, fast, S)
+         f"fast={fast} S={S} out={out} profile={profile}")
+    y, acc = gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile)
+    acc_o, y_o = oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile)
     assert_same(acc, acc_o, what + " accumulator")
     assert_same(y, y_o, what + " output")
 
@@ -176,11 +177,14 @@ def test_large_tiles(dev, orc, fast, S):
     check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.1, 1 / 3, "bf16", fast, S, f"large tiles fast={fast} S={S}")
 
 
+@pytest.mark.parametrize("profile", ["hopper", "ada-pairwise"])
 @pytest.mark.parametrize("cfg", range(8))
 @pytest.mark.parametrize("shape", [(1, 16, 48), (37, 80, 400), (70, 144, 1040)])
-def test_every_tile_config(dev, orc, cfg, shape):
+def test_every_tile_config(dev, orc, cfg, shape, profile):
     """Every tile configuration (including 2 and 4 lanes per output) gives the
-    oracle's bits, fast and slow, unsplit and split, on ragged shapes."""
+    oracle's bits, fast and slow, unsplit and split, on ragged shapes, with
+    32-product blocks (hopper) and 16-product blocks over round-robin splits
+    (ada)."""
     M, N, K = shape
     gen = torch.Generator().manual_seed(100 + cfg)
     x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
@@ -189,9 +193,55 @@ def test_every_tile_config(dev, orc, cfg, shape):
     try:
         for fast, S in ((True, 1), (False, 1), (True, 3), (False, 2)):
             check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, "bf16", fast, S,
-                  f"tile {api.TILE_CONFIGS[cfg]} {shape}")
+                  f"tile {api.TILE_CONFIGS[cfg]} {shape}", profile=profile)
     finally:
         api.force_tile(prev)
+
+
+# ---- the RTX 4060 (ada) profiles ------------------------------------------------
+@pytest.mark.parametrize("name,seed,profile", [
+    ("tiny", 0, "ada-serial"), ("tiny", 1, "ada-pairwise"),
+    ("proj_64x5760x1920", 0, "ada-serial"),
+    ("slow_256x4096x4096", 0, "ada-pairwise"),
+    ("splitk_16x256x65536_s8", 0, "ada-serial"), ("splitk_16x256x65536_s8", 1, "ada-pairwise"),
+])
+def test_ada_workload_full(dev, orc, name, seed, profile):
+    """The workloads under the RTX 4060 profiles: 16-product blocks, 64-wide
+    k-tiles dealt round-robin to the splits, serial or pairwise combination."""
+    wl = WORKLOADS[name]
+    x, w = make_operands(wl, seed)
+    check(dev, orc, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S,
+          f"{name} seed {seed}", profile=profile)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_ada_edge_cases(dev, orc, seed):
+    """The edge-case sweep (ragged sizes, K = 0, empty splits, specials, every
+    output type) under the ada profiles, with split counts from 1 to 17 so
+    that the pairwise tree has absent leaves and the round-robin layout has
+    splits of unequal length and a short last tile."""
+    x, xfmt, w, wfmt, sx, sw, out, fast, S = _edge_case(1000 + seed)
+    S = [1, 2, 3, 4, 5, 7, 8, 9, 16, 17][seed % 10]
+    profile = ("ada-serial", "ada-pairwise")[seed % 2]
+    check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, f"ada edge case {seed}", profile=profile)
+
+
+def test_ada_large_sampled(dev, orc):
+    """A 2048 x 2048 x 8192 e4m3 x e5m2 problem (the matrix-core exponent
+    path at size) under ada-pairwise with S = 3, on sampled outputs."""
+    wl = Workload("ada_large", 2048, 2048, 8192, "e4m3fn", "e5m2", 40.0, 1000.0, 0.01, 0.01,
+                  1 / 256, 1 / 256, True, 3, "bf16")
+    x, w = make_operands(wl, 0)
+    note("[gpu] ada_large: full-size run")
+    y, acc = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S,
+                     profile="ada-pairwise")
+    rng = np.random.default_rng(1)
+    ms = np.array(list(rng.integers(0, wl.M, 600)) + [0, wl.M - 1, 63, 64], dtype=np.int64)
+    ns = np.array(list(rng.integers(0, wl.N, 600)) + [wl.N - 1, 0, 64, 63], dtype=np.int64)
+    acc_o, y_o = orc.points(x.numpy(), wl.xfmt, w.numpy(), wl.wfmt, ms, ns, scale_bits(wl.scale_x),
+                            scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S, profile="ada-pairwise")
+    assert_same(acc[ms, ns], acc_o, "ada_large accumulator")
+    assert_same(y[ms, ns], y_o, "ada_large output")
 
 
 # ---- invariants -------------------------------------------------------------------
