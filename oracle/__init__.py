@@ -26,7 +26,8 @@ SOURCE = os.path.join(HERE, "emu_oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 FMT = {"e4m3fn": 0, "e5m2": 1}
-OUT = {"bf16": 0, "fp16": 1, "fp32": 2}
+OUT = {"bf16": 0, "fp16": 1, "fp32": 2, "e4m3fn": 3, "e5m2": 4}
+ONE = 0x3F800000  # binary32 1.0: the default scale_result
 CLS_ZERO, CLS_FINITE, CLS_INF, CLS_NAN = 0, 1, 2, 3
 
 LAYOUT = {"contiguous": 0, "round-robin": 1}
@@ -87,7 +88,7 @@ class Oracle:
             getattr(L, name).restype = ctypes.c_uint32
         L.oracle_encode_output.argtypes = [ctypes.c_uint32, ctypes.c_int]
         L.oracle_encode_output.restype = ctypes.c_uint32
-        L.oracle_output_from_acc.argtypes = [ctypes.c_uint32] * 3 + [ctypes.c_int]
+        L.oracle_output_from_acc.argtypes = [ctypes.c_uint32] * 4 + [ctypes.c_int]
         L.oracle_output_from_acc.restype = ctypes.c_uint32
         L.oracle_chain_exact.argtypes = [
             _U8P, ctypes.c_int, ctypes.c_int64, _U8P, ctypes.c_int, ctypes.c_int64,
@@ -97,14 +98,14 @@ class Oracle:
                                         ctypes.c_int64, ctypes.c_int, _IP, _I64P, _IP]
         L.oracle_points.argtypes = [
             _U8P, ctypes.c_int, ctypes.c_int64, _U8P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-            ctypes.c_int64, _I64P, _I64P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, _I64P, _I64P, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            _U32P, _U32P]
+            ctypes.c_int, _U32P, _U32P]
         L.oracle_scaled_mm.argtypes = [
             _U8P, ctypes.c_int, ctypes.c_int64, _U8P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            _U32P, _U32P, ctypes.c_int]
+            ctypes.c_int, _U32P, _U32P, ctypes.c_int]
 
     @property
     def mutant(self) -> int:
@@ -128,8 +129,8 @@ class Oracle:
     def encode_output(self, y32: int, out: str) -> int:
         return self.lib.oracle_encode_output(y32, OUT[out])
 
-    def output_from_acc(self, acc: int, sx: int, sw: int, out: str) -> int:
-        return self.lib.oracle_output_from_acc(acc, sx, sw, OUT[out])
+    def output_from_acc(self, acc: int, sx: int, sw: int, out: str, sr: int = ONE) -> int:
+        return self.lib.oracle_output_from_acc(acc, sx, sw, sr, OUT[out])
 
     def block_step(self, prods, F=13, c=(0, 0, 0)):
         """prods: list of (sign, g, P); c: (neg, mag, q).  Returns (neg, mag, q)."""
@@ -153,9 +154,10 @@ class Oracle:
 
     # ---- matrix entry points -------------------------------------------
     def scaled_mm(self, x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1,
-                  profile=None, threads=None):
+                  profile=None, threads=None, sr_bits=ONE):
         """x: uint8 [M,K], w: uint8 [N,K] (codes).  Returns (acc uint32 [M,N],
-        y uint32 [M,N] holding the output bit patterns)."""
+        y uint32 [M,N] holding the output bit patterns).  sr_bits: the
+        binary32 scale_result, used by FP8 outputs only."""
         pf = resolve_profile(profile)
         x = np.ascontiguousarray(x, dtype=np.uint8)
         w = np.ascontiguousarray(w, dtype=np.uint8)
@@ -166,7 +168,7 @@ class Oracle:
         y = np.zeros((M, N), dtype=np.uint32)
         threads = threads or os.cpu_count() or 1
         rc = self.lib.oracle_scaled_mm(_u8(x), FMT[xfmt], max(K, 1), _u8(w), FMT[wfmt], max(K, 1),
-                                       M, N, K, sx_bits, sw_bits, OUT[out], int(fast), S,
+                                       M, N, K, sx_bits, sw_bits, sr_bits, OUT[out], int(fast), S,
                                        pf["B"], pf["F"], pf["Q"], pf["W"], LAYOUT[pf["layout"]],
                                        COMBINE[pf["combine"]], _u32(acc), _u32(y), threads)
         if rc != 0:
@@ -174,7 +176,7 @@ class Oracle:
         return acc, y
 
     def points(self, x, xfmt, w, wfmt, ms, ns, sx_bits, sw_bits, out="bf16", fast=True, S=1,
-               profile=None):
+               profile=None, sr_bits=ONE):
         """Accumulator and output at the listed (m, n) points only."""
         pf = resolve_profile(profile)
         x = np.ascontiguousarray(x, dtype=np.uint8)
@@ -186,7 +188,7 @@ class Oracle:
         y = np.zeros(len(ms), dtype=np.uint32)
         rc = self.lib.oracle_points(_u8(x), FMT[xfmt], max(K, 1), _u8(w), FMT[wfmt], max(K, 1), K,
                                     len(ms), ms.ctypes.data_as(_I64P), ns.ctypes.data_as(_I64P),
-                                    sx_bits, sw_bits, OUT[out], int(fast), S,
+                                    sx_bits, sw_bits, sr_bits, OUT[out], int(fast), S,
                                     pf["B"], pf["F"], pf["Q"], pf["W"], LAYOUT[pf["layout"]],
                                     COMBINE[pf["combine"]], _u32(acc), _u32(y))
         if rc != 0:

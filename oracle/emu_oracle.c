@@ -60,11 +60,13 @@
 #define MUT_RR_AS_CONTIGUOUS  18  /* round-robin split layout taken as contiguous runs */
 #define MUT_PAIRWISE_ADJACENT 19  /* pairwise combination over adjacent pairs, ((p0+p1)+p2)... */
 #define MUT_RR_TILE_DOUBLED   20  /* round-robin k-tiles twice as wide as the profile's */
+#define MUT_SR_FOLDED         21  /* scale_result folded into alpha instead of a separate multiply */
+#define MUT_FP8_NO_SATURATION 22  /* FP8 outputs overflow to NaN / Inf instead of saturating */
 
 /* ------------------------------------------------------------------------ */
 /* Public constants (mirrored in oracle/__init__.py).                        */
 enum { FMT_E4M3FN = 0, FMT_E5M2 = 1 };
-enum { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2 };
+enum { OUT_BF16 = 0, OUT_FP16 = 1, OUT_FP32 = 2, OUT_E4M3FN = 3, OUT_E5M2 = 4 };
 enum { CLS_ZERO = 0, CLS_FINITE = 1, CLS_INF = 2, CLS_NAN = 3 };
 
 enum { LAYOUT_CONTIGUOUS = 0, LAYOUT_ROUND_ROBIN = 1 };
@@ -585,6 +587,9 @@ static float f32_from(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 #define CANON_NAN_F32 0x7FFFFFFFu
 #define CANON_NAN_16 0x7FFFu
 #endif
+/* Reading: the FP8 NaN output is 0x7F for both formats (all exponent and
+ * mantissa bits set; a NaN in e4m3fn and in e5m2).  Parity unpinned. */
+#define CANON_NAN_8 0x7Fu
 
 /* binary32 product RN32(a*b) of two binary32 values (IEEE multiplication). */
 static float mul_f32(float a, float b)
@@ -665,6 +670,39 @@ static uint32_t encode_single_rounded(float acc, float alpha, int out_dtype)
 }
 #endif
 
+/*
+ * FP8 outputs (validation page, scope table row "Epilogue": fp8 output with
+ * scale_result and saturation; claims table: scale_result is a separate fp32
+ * multiply before saturation to the format's maximum):
+ *   y' = RN32(y32 * scale_result), a plain IEEE binary32 multiplication;
+ *   |y'| is clamped to the format's largest finite value (448 for e4m3fn,
+ *   57344 for e5m2), infinities included;
+ *   the result is rounded to nearest even in the format, subnormals kept,
+ *   the sign of a zero kept.
+ * Reading: clamping before the rounding equals rounding with saturation,
+ * because the largest finite value is representable.
+ */
+static uint32_t encode_fp8(float y, int out_dtype)
+{
+    const int e4 = out_dtype == OUT_E4M3FN;
+    const int p = e4 ? 4 : 3, emin = e4 ? -6 : -14, bias = e4 ? 7 : 15, mb = p - 1;
+    const double maxv = e4 ? 448.0 : 57344.0;
+    if (isnan(y)) return CANON_NAN_8;
+    uint32_t sign = signbit(y) ? 0x80u : 0u;
+    double a = fabs((double)y);
+#if ORACLE_MUTANT == MUT_FP8_NO_SATURATION
+    if (a > maxv) return e4 ? (sign | 0x7Fu) : (sign | 0x7Cu);
+#endif
+    if (a > maxv) a = maxv;
+    double r = round_to_format(a, p, emin, e4 ? 8 : 15);
+    if (r == 0.0) return sign;
+    int e;
+    frexp(r, &e);
+    e -= 1;
+    if (e < emin) return sign | (uint32_t)(r / ldexp(1.0, emin - mb));
+    return sign | ((uint32_t)(e + bias) << mb) | ((uint32_t)(r / ldexp(1.0, e - mb)) - (1u << mb));
+}
+
 /* ------------------------------------------------------------------------ */
 /* Exported entry points. */
 
@@ -683,8 +721,15 @@ static uint32_t acc_bits_at(const operands *o, int64_t m, int64_t n, int fast, i
     return f32_bits(finite_accumulator(o, m, n, fast, S, pf));
 }
 
-static uint32_t out_bits_from_acc(uint32_t acc_bits, float alpha, int out_dtype)
+static uint32_t out_bits_from_acc(uint32_t acc_bits, float alpha, float scale_result, int out_dtype)
 {
+    if (out_dtype == OUT_E4M3FN || out_dtype == OUT_E5M2) {
+#if ORACLE_MUTANT == MUT_SR_FOLDED
+        return encode_fp8(epilogue_f32(f32_from(acc_bits), mul_f32(alpha, scale_result)), out_dtype);
+#else
+        return encode_fp8(mul_f32(epilogue_f32(f32_from(acc_bits), alpha), scale_result), out_dtype);
+#endif
+    }
 #if ORACLE_MUTANT == MUT_SINGLE_ROUNDING
     return encode_single_rounded(f32_from(acc_bits), alpha, out_dtype);
 #else
@@ -715,13 +760,20 @@ API uint32_t oracle_epilogue_f32(uint32_t acc, uint32_t alpha)
     return isnan(y) ? CANON_NAN_F32 : f32_bits(y);
 }
 
-API uint32_t oracle_encode_output(uint32_t y32, int out_dtype) { return encode_output(f32_from(y32), out_dtype); }
+/* The last rounding alone: y32 (for FP8 outputs: y32 * scale_result) to the
+ * output format. */
+API uint32_t oracle_encode_output(uint32_t y32, int out_dtype)
+{
+    if (out_dtype == OUT_E4M3FN || out_dtype == OUT_E5M2) return encode_fp8(f32_from(y32), out_dtype);
+    return encode_output(f32_from(y32), out_dtype);
+}
 
-/* Full epilogue: alpha = RN32(sx*sw), then y = out(RN32(acc*alpha)). */
-API uint32_t oracle_output_from_acc(uint32_t acc_bits, uint32_t sx, uint32_t sw, int out_dtype)
+/* Full epilogue: alpha = RN32(sx*sw), then y = out(RN32(acc*alpha)); FP8
+ * outputs multiply by scale_result (sr) in between. */
+API uint32_t oracle_output_from_acc(uint32_t acc_bits, uint32_t sx, uint32_t sw, uint32_t sr, int out_dtype)
 {
     float alpha = mul_f32(f32_from(sx), f32_from(sw));
-    return out_bits_from_acc(acc_bits, alpha, out_dtype);
+    return out_bits_from_acc(acc_bits, alpha, f32_from(sr), out_dtype);
 }
 
 /* The exact chain of [k0, k1) for one output, starting from +0 (no specials,
@@ -756,8 +808,10 @@ API int oracle_block_step(const int *g, const int *P, const int *s, int n, int F
     return 0;
 }
 
-static int check_args(int B, int F, int S, int Q, int W, int layout, int combine, int xfmt, int wfmt)
+static int check_args(int B, int F, int S, int Q, int W, int layout, int combine, int xfmt, int wfmt,
+                      int out_dtype)
 {
+    if (out_dtype < OUT_BF16 || out_dtype > OUT_E5M2) return -1;
     if (B < 1 || B > MAX_B || F < 1 || F > 23) return -1;
     if (S < 1 || S > 4096 || Q < 1 || W < 1) return -1;
     if ((layout != LAYOUT_CONTIGUOUS && layout != LAYOUT_ROUND_ROBIN) ||
@@ -769,17 +823,17 @@ static int check_args(int B, int F, int S, int Q, int W, int layout, int combine
 /* Accumulator and output at a list of (m, n) points. */
 API int oracle_points(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt, int64_t ldw,
                       int64_t K, int64_t npts, const int64_t *ms, const int64_t *ns, uint32_t sx,
-                      uint32_t sw, int out_dtype, int fast, int S, int B, int F, int Q, int W,
+                      uint32_t sw, uint32_t sr, int out_dtype, int fast, int S, int B, int F, int Q, int W,
                       int layout, int combine, uint32_t *acc_out, uint32_t *y_out)
 {
-    if (check_args(B, F, S, Q, W, layout, combine, xfmt, wfmt)) return -1;
+    if (check_args(B, F, S, Q, W, layout, combine, xfmt, wfmt, out_dtype)) return -1;
     operands o = {x, xfmt, ldx, w, wfmt, ldw, 0, 0, K};
     oracle_profile pf = {B, F, Q, W, layout, combine};
     float alpha = mul_f32(f32_from(sx), f32_from(sw));
     for (int64_t i = 0; i < npts; i++) {
         uint32_t a = acc_bits_at(&o, ms[i], ns[i], fast, S, &pf);
         if (acc_out) acc_out[i] = a;
-        if (y_out) y_out[i] = out_bits_from_acc(a, alpha, out_dtype);
+        if (y_out) y_out[i] = out_bits_from_acc(a, alpha, f32_from(sr), out_dtype);
     }
     return 0;
 }
@@ -787,7 +841,7 @@ API int oracle_points(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w,
 typedef struct {
     const operands *o;
     const oracle_profile *pf;
-    float alpha;
+    float alpha, scale_result;
     int out_dtype, fast, S;
     uint32_t *acc_out, *y_out;
     int64_t row_begin, row_end;
@@ -800,20 +854,21 @@ static void *run_rows(void *arg)
         for (int64_t n = 0; n < j->o->N; n++) {
             uint32_t a = acc_bits_at(j->o, m, n, j->fast, j->S, j->pf);
             if (j->acc_out) j->acc_out[m * j->o->N + n] = a;
-            if (j->y_out) j->y_out[m * j->o->N + n] = out_bits_from_acc(a, j->alpha, j->out_dtype);
+            if (j->y_out) j->y_out[m * j->o->N + n] = out_bits_from_acc(a, j->alpha, j->scale_result, j->out_dtype);
         }
     return NULL;
 }
 
 /* The whole [M, N] result, rows spread over nthreads host threads.
  * acc_out and y_out are dense [M, N] arrays of bit patterns (either may be
- * NULL).  y_out holds 16-bit patterns in the low half for bf16/fp16. */
+ * NULL).  y_out holds 16-bit patterns in the low half for bf16/fp16 and
+ * 8-bit patterns in the low byte for FP8 outputs. */
 API int oracle_scaled_mm(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt,
                          int64_t ldw, int64_t M, int64_t N, int64_t K, uint32_t sx, uint32_t sw,
-                         int out_dtype, int fast, int S, int B, int F, int Q, int W, int layout,
+                         uint32_t sr, int out_dtype, int fast, int S, int B, int F, int Q, int W, int layout,
                          int combine, uint32_t *acc_out, uint32_t *y_out, int nthreads)
 {
-    if (check_args(B, F, S, Q, W, layout, combine, xfmt, wfmt)) return -1;
+    if (check_args(B, F, S, Q, W, layout, combine, xfmt, wfmt, out_dtype)) return -1;
     if (M < 0 || N < 0 || K < 0) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -825,7 +880,7 @@ API int oracle_scaled_mm(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t 
     int nt = (int)((M < nthreads) ? (M > 0 ? M : 1) : nthreads);
     int64_t per = (M + nt - 1) / nt;
     for (int t = 0; t < nt; t++) {
-        jobs[t].o = &o; jobs[t].pf = &pf; jobs[t].alpha = alpha;
+        jobs[t].o = &o; jobs[t].pf = &pf; jobs[t].alpha = alpha; jobs[t].scale_result = f32_from(sr);
         jobs[t].out_dtype = out_dtype; jobs[t].fast = fast; jobs[t].S = S;
         jobs[t].acc_out = acc_out; jobs[t].y_out = y_out;
         jobs[t].row_begin = t * per < M ? t * per : M;

@@ -218,8 +218,34 @@ def encode16(v, fmt, negative_zero=False) -> int:
     return sign | ((e + bias) << mbits) | int(m)
 
 
-def epilogue_bits(acc_bits: int, sx_bits: int, sw_bits: int, out: str) -> int:
-    """alpha = RN32(sx*sw); y32 = RN32(acc*alpha + (+0)); then RN to the output."""
+E4M3FN = (4, -6, 8)
+E5M2 = (3, -14, 15)
+FP8_MAX = {"e4m3fn": Fraction(448), "e5m2": Fraction(57344)}
+CANON_NAN_8 = 0x7F
+
+
+def encode8(v, out, negative_zero=False) -> int:
+    """Bits of a value exactly representable in the FP8 output format."""
+    p, emin, _ = E4M3FN if out == "e4m3fn" else E5M2
+    bias, mbits = (7, 3) if out == "e4m3fn" else (15, 2)
+    sign = 0x80 if (v < 0 or (v == 0 and negative_zero)) else 0
+    if v == 0:
+        return sign
+    a = abs(v)
+    e = floor_log2(a)
+    if e < emin:
+        m = a / Fraction(2) ** (emin - mbits)
+        assert m.denominator == 1
+        return sign | int(m)
+    m = a / Fraction(2) ** (e - mbits) - (1 << mbits)
+    assert m.denominator == 1
+    return sign | ((e + bias) << mbits) | int(m)
+
+
+def epilogue_bits(acc_bits: int, sx_bits: int, sw_bits: int, out: str, sr_bits: int = 0x3F800000) -> int:
+    """alpha = RN32(sx*sw); y32 = RN32(acc*alpha + (+0)); then RN to the output.
+    FP8 outputs: y' = RN32(y32 * scale_result), |y'| clamped to the format's
+    largest finite value, then RN to the format."""
     acc, sx, sw = f32_value(acc_bits), f32_value(sx_bits), f32_value(sw_bits)
     neg_sx, neg_sw = bool(sx_bits >> 31), bool(sw_bits >> 31)
 
@@ -243,6 +269,7 @@ def epilogue_bits(acc_bits: int, sx_bits: int, sw_bits: int, out: str) -> int:
     # y32
     acc_neg = bool(acc_bits >> 31)
     y_neg_zero = False
+    y = None
     if nan or is_nan(acc) or (is_inf(acc) and alpha == 0) or (is_inf(alpha) and acc == 0):
         nan = True
     elif is_inf(acc) or is_inf(alpha):
@@ -254,6 +281,27 @@ def epilogue_bits(acc_bits: int, sx_bits: int, sw_bits: int, out: str) -> int:
         else:
             y = round_nearest_even(exact)
             y_neg_zero = (y == 0) and exact < 0
+    if out in FP8_MAX:
+        if nan:
+            return CANON_NAN_8
+        sr = f32_value(sr_bits)
+        sr_neg = bool(sr_bits >> 31)
+        y_neg = (y < 0) or y_neg_zero
+        if is_nan(sr) or (is_inf(y) and sr == 0) or (y == 0 and is_inf(sr)):
+            return CANON_NAN_8
+        if is_inf(y) or is_inf(sr):
+            yp, yp_negzero = (-math.inf if (y_neg ^ sr_neg) else math.inf), False
+        else:
+            exact = y * sr
+            if exact == 0:
+                yp, yp_negzero = Fraction(0), y_neg ^ sr_neg
+            else:
+                yp = round_nearest_even(exact)
+                yp_negzero = (yp == 0) and exact < 0
+        neg = (yp < 0) or yp_negzero
+        a = FP8_MAX[out] if is_inf(yp) else min(abs(yp), FP8_MAX[out])
+        r = round_nearest_even(a, E4M3FN if out == "e4m3fn" else E5M2)
+        return encode8(-r if neg else r, out, negative_zero=neg)
     if out == "fp32":
         return CANON_NAN_32 if nan else f32_bits_of(y, y_neg_zero)
     if nan:
@@ -326,7 +374,7 @@ def accumulator_bits(*args, **kw) -> int:
 
 
 def scaled_mm(x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1, B=32, F=13, Q=128, W=128,
-              layout="contiguous", scheme="serial"):
+              layout="contiguous", scheme="serial", sr_bits=0x3F800000):
     """Tiny whole-matrix evaluation: returns (acc bits, output bits) as lists of lists."""
     M, K = len(x), (len(x[0]) if len(x) else 0)
     N = len(w)
@@ -336,7 +384,7 @@ def scaled_mm(x, xfmt, w, wfmt, sx_bits, sw_bits, out="bf16", fast=True, S=1, B=
         for n in range(N):
             a = accumulator_bits(x[m], xfmt, w[n], wfmt, K, fast, S, B, F, Q, W, layout, scheme)
             ra.append(a)
-            ry.append(epilogue_bits(a, sx_bits, sw_bits, out))
+            ry.append(epilogue_bits(a, sx_bits, sw_bits, out, sr_bits))
         accs.append(ra)
         ys.append(ry)
     return accs, ys

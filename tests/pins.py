@@ -48,8 +48,15 @@ def bits32(v) -> np.ndarray:
     return np.asarray(v, dtype=np.float32).view(np.uint32)
 
 
-def independent_epilogue(acc_bits, sx_bits, sw_bits, out: str) -> np.ndarray:
+FP8_MAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
+
+
+def independent_epilogue(acc_bits, sx_bits, sw_bits, out: str, sr_bits=0x3F800000) -> np.ndarray:
     """y = out(RN32(acc * RN32(sx*sw) + (+0))) with numpy / torch IEEE routines.
+
+    FP8 outputs: a numpy binary32 multiplication by scale_result, numpy's
+    clip to the format's largest finite value (infinities included), then
+    torch's round-to-nearest-even conversion to the FP8 format; NaN -> 0x7F.
 
     alpha is a numpy binary32 multiplication; acc*alpha is exact in float64
     (24 x 24 bits) and numpy's float64 -> float32 conversion rounds it once to
@@ -63,6 +70,13 @@ def independent_epilogue(acc_bits, sx_bits, sw_bits, out: str) -> np.ndarray:
         y32 = prod.astype(np.float32)
     y32 = np.where(prod == 0, np.float32(0.0), y32)
     nan = np.isnan(y32)
+    if out in FP8_MAX:
+        with np.errstate(all="ignore"):
+            yp = y32.astype(np.float32) * np.float32(f32(sr_bits))
+        yp = np.clip(yp, np.float32(-FP8_MAX[out]), np.float32(FP8_MAX[out]))
+        b = torch.from_numpy(np.ascontiguousarray(yp)).to(TORCH_FP8[out]).view(torch.uint8)
+        b = b.numpy().astype(np.uint32)
+        return np.where(np.isnan(yp), np.uint32(0x7F), b).astype(np.uint32)
     if out == "fp32":
         return np.where(nan, np.uint32(CANON32), bits32(y32)).astype(np.uint32)
     if out == "bf16":
@@ -99,15 +113,16 @@ def pin_golden(o):
         sx = int(c.get("scale_x", "0x3F800000"), 16)
         sw = int(c.get("scale_w", "0x3F800000"), 16)
         out = c.get("out", "fp32")
+        sr = int(c.get("scale_result", "0x3F800000"), 16)
         acc, y = o.scaled_mm(x, c["xfmt"], w, c["wfmt"], sx, sw, out, c["fast"], c["S"],
-                             profile=c.get("profile", "hopper"))
+                             profile=c.get("profile", "hopper"), sr_bits=sr)
         assert int(acc[0, 0]) == int(c["acc"], 16), (c["id"], hex(int(acc[0, 0])), c["acc"])
         if "y" in c:
             assert int(y[0, 0]) == int(c["y"], 16), (c["id"], hex(int(y[0, 0])), c["y"])
 
 
 def pin_code_pairs(o, pairs=(("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn")),
-                   outs=("bf16", "fp16", "fp32")):
+                   outs=("bf16", "fp16", "fp32", "e4m3fn", "e5m2")):
     """Every pair of FP8 codes as the only nonzero product of a K=16 row
     (validation page, claims table: every pair of FP8 codes through the GEMM
     epilogue).  A single product never exceeds 8 significant bits, so the
@@ -128,10 +143,11 @@ def pin_code_pairs(o, pairs=(("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", 
         exp_acc = np.where(np.isnan(prod), np.uint32(CANON32), exp_acc)
         exp_acc = np.where(prod == 0, np.uint32(0), exp_acc)
         sx, sw = 0x3EAAAAAB, 0x3DCCCCCD  # RN32(1/3), RN32(0.1): non-power-of-two scales
+        sr = 0x4119999A  # RN32(9.6): FP8 outputs reach saturation, ties and subnormals
         for out in outs:
-            acc, y = o.scaled_mm(x, xf, w, wf, sx, sw, out, True, 1)
+            acc, y = o.scaled_mm(x, xf, w, wf, sx, sw, out, True, 1, sr_bits=sr)
             assert np.array_equal(acc, exp_acc), (xf, wf, "acc", _first_diff(acc, exp_acc))
-            ey = independent_epilogue(exp_acc, sx, sw, out)
+            ey = independent_epilogue(exp_acc, sx, sw, out, sr)
             assert np.array_equal(y, ey), (xf, wf, out, _first_diff(y, ey))
 
 
@@ -363,23 +379,28 @@ def pin_epilogue_random(o, n=20000, seed=23):
     for out in ("bf16", "fp16", "fp32"):
         got = np.array([o.output_from_acc(int(a), int(b), int(c), out) for a, b, c in zip(acc, sx, sw)],
                        dtype=np.uint32)
-        accf = f32(acc).astype(np.float64)
-        with np.errstate(all="ignore"):
-            alpha = (f32(sx) * f32(sw)).astype(np.float64)
-            prod = accf * alpha
-            y32 = prod.astype(np.float32)
-        y32 = np.where(prod == 0, np.float32(0.0), y32)
-        nan = np.isnan(y32)
-        if out == "fp32":
-            want = np.where(nan, np.uint32(CANON32), bits32(y32))
-        elif out == "bf16":
-            b = torch.from_numpy(np.ascontiguousarray(y32)).to(torch.bfloat16).view(torch.int16)
-            want = np.where(nan, np.uint32(CANON16), b.numpy().astype(np.uint16).astype(np.uint32))
-        else:
-            with np.errstate(all="ignore"):
-                h = y32.astype(np.float16).view(np.uint16).astype(np.uint32)
-            want = np.where(nan, np.uint32(CANON16), h)
+        want = independent_epilogue(acc, sx, sw, out)
         assert np.array_equal(got, want.astype(np.uint32)), (out, _first_diff(got, want))
+    # FP8 outputs: random scale_result (including zeros, infinities, NaN and
+    # negative values), plus accumulators on e4m3 / e5m2 ties (alpha = 1,
+    # scale_result = 1) across the normal and subnormal ranges
+    sr = np.where(rng.random(len(acc)) < 0.3, np.uint32(0x3F800000),
+                  rng.integers(0x30000000, 0x50000000, len(acc), dtype=np.int64).astype(np.uint32))
+    sr[:len(specials)] = specials
+    sr[::5] |= np.uint32(0x80000000)
+    ties8 = np.concatenate([
+        (rng.integers(0x3A000000, 0x44000000, 1000, dtype=np.int64).astype(np.uint32) & np.uint32(0xFFF00000))
+        | np.uint32(0x00080000),
+        (rng.integers(0x34000000, 0x48000000, 1000, dtype=np.int64).astype(np.uint32) & np.uint32(0xFFE00000))
+        | np.uint32(0x00100000)])
+    ones = np.full(len(ties8), 0x3F800000, dtype=np.uint32)
+    acc8, sx8, sw8, sr8 = (np.concatenate([acc, ties8]), np.concatenate([sx, ones]),
+                           np.concatenate([sw, ones]), np.concatenate([sr, ones]))
+    for out in ("e4m3fn", "e5m2"):
+        got = np.array([o.output_from_acc(int(a), int(b), int(c), out, int(d))
+                        for a, b, c, d in zip(acc8, sx8, sw8, sr8)], dtype=np.uint32)
+        want = independent_epilogue(acc8, sx8, sw8, out, sr8)
+        assert np.array_equal(got, want), (out, _first_diff(got, want))
 
 
 def pin_spec_cross_check(o, trials=1500, seed=29):

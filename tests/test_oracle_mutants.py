@@ -31,6 +31,8 @@ MUTANTS = {
     18: "round-robin split layout taken as contiguous runs",
     19: "pairwise combination over adjacent pairs",
     20: "round-robin k-tiles twice as wide",
+    21: "scale_result folded into alpha",
+    22: "FP8 outputs overflow instead of saturating",
 }
 
 
