@@ -168,7 +168,7 @@ def main():
         api.force_tile(args.tile)
     stream = torch.cuda.current_stream(dev)
     call_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
-                 wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), out.data_ptr(), api.OUT_DTYPE[out.dtype],
+                 wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), None, out.data_ptr(), api.OUT_DTYPE[out.dtype],
                  wl.N, int(wl.fast), wl.split_S, api.PROFILE[args.profile], wsbuf.data_ptr(), ws_bytes,
                  stream.cuda_stream)
 

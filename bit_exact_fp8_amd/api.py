@@ -22,7 +22,8 @@ _LIBNAME = "libemu_fp8gemm.so"
 EMU_OK, EMU_ERR_INVALID_ARG, EMU_ERR_REJECTED, EMU_ERR_UNSUPPORTED, EMU_ERR_WORKSPACE, EMU_ERR_DEVICE = range(6)
 FP8_FORMAT = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
 FP8_FORMAT_NAME = {"e4m3fn": 0, "e5m2": 1}
-OUT_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+OUT_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2, torch.float8_e4m3fn: 3,
+             torch.float8_e5m2: 4}
 PROFILE = {"hopper": 0, "ada-serial": 1, "ada-pairwise": 2}
 
 
@@ -52,7 +53,7 @@ def _lib():
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     common = [vp, i32, i64, vp, i32, i64, i64, i64, i64]
-    lib.emu_scaled_mm.argtypes = common + [vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.emu_scaled_mm.argtypes = common + [vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.emu_scaled_mm.restype = i32
     lib.emu_accumulate.argtypes = common + [vp, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.emu_accumulate.restype = i32
@@ -132,11 +133,14 @@ def _operands(mat1, mat2):
 
 def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
               out_dtype=None, use_fast_accum: bool = False, split_S: int = 1,
-              profile: str = "hopper", out: torch.Tensor | None = None) -> torch.Tensor:
+              profile: str = "hopper", out: torch.Tensor | None = None,
+              scale_result: torch.Tensor | None = None) -> torch.Tensor:
     """y = (mat1 @ mat2) * scale_a * scale_b with the emulated FP8 arithmetic.
 
     Defaults follow torch (user guide, section 3): use_fast_accum=False and
-    out_dtype = the input dtype (FP8 outputs are not built and raise)."""
+    out_dtype = the input dtype.  scale_result (FP8 outputs only) is a
+    one-element float32 tensor multiplied in before the saturating FP8
+    conversion."""
     x, w, M, N, K, ldx, ldw = _operands(mat1, mat2)
     if out_dtype is None:
         out_dtype = mat1.dtype
@@ -151,8 +155,9 @@ def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, sca
     ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
     wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     lib = _lib()
+    sr = _scale_ptr(scale_result, dev) if scale_result is not None else None
     _check(lib.emu_scaled_mm(x.data_ptr(), _fmt(x), ldx, w.data_ptr(), _fmt(w), ldw, M, N, K,
-                             _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), out.data_ptr(),
+                             _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), sr, out.data_ptr(),
                              OUT_DTYPE[out_dtype], ldo, int(use_fast_accum), int(split_S),
                              PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev)))
     return out

@@ -122,7 +122,8 @@ emu_status check_common(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const 
 }
 
 emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w, emu_fp8_format wf,
-               int64_t ldw, int64_t M, int64_t N, int64_t K, const float *sx, const float *sw, void *out,
+               int64_t ldw, int64_t M, int64_t N, int64_t K, const float *sx, const float *sw,
+               const float *sr, void *out,
                int out_kind, size_t out_elem, int64_t ldo, int fast, int S, emu_profile profile,
                void *workspace, size_t workspace_bytes, void *stream_ptr)
 {
@@ -144,6 +145,7 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
     p.fast = fast ? 1 : 0;
     p.scale_x = sx;
     p.scale_w = sw;
+    p.scale_result = sr;
     p.w = w;
     if (S == 1) {
         p.out_kind = out_kind;
@@ -177,6 +179,7 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
         c.ldo = ldo;
         c.scale_x = sx;
         c.scale_w = sw;
+        c.scale_result = sr;
         hipError_t e = emu::launch_combine(c, stream);
         if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("combine kernel launch: ") + hipGetErrorString(e));
     }
@@ -200,9 +203,9 @@ size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fas
 
 emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
                          emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K,
-                         const float *scale_x, const float *scale_w, void *out, emu_out_dtype out_dtype,
-                         int64_t ldo, int fast_accum, int split_S, emu_profile profile, void *workspace,
-                         size_t workspace_bytes, void *stream)
+                         const float *scale_x, const float *scale_w, const float *scale_result, void *out,
+                         emu_out_dtype out_dtype, int64_t ldo, int fast_accum, int split_S, emu_profile profile,
+                         void *workspace, size_t workspace_bytes, void *stream)
 {
     emu_status s = check_common(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, split_S, profile);
     if (s != EMU_OK) return s;
@@ -212,11 +215,14 @@ emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, co
     case EMU_OUT_BF16: kind = emu::OUT_BF16; elem = 2; break;
     case EMU_OUT_FP16: kind = emu::OUT_F16; elem = 2; break;
     case EMU_OUT_FP32: kind = emu::OUT_F32; elem = 4; break;
-    default:
-        if ((int)out_dtype >= 3 && (int)out_dtype <= 4)
-            return fail(EMU_ERR_UNSUPPORTED, "FP8 outputs are not built");
-        return fail(EMU_ERR_INVALID_ARG, "unknown output dtype");
+    case EMU_OUT_E4M3FN: kind = emu::OUT_E4M3; elem = 1; break;
+    case EMU_OUT_E5M2: kind = emu::OUT_E5M2; elem = 1; break;
+    default: return fail(EMU_ERR_INVALID_ARG, "unknown output dtype");
     }
+    const bool fp8_out = kind == emu::OUT_E4M3 || kind == emu::OUT_E5M2;
+    if (scale_result && !fp8_out) return fail(EMU_ERR_UNSUPPORTED, "scale_result is for FP8 outputs only");
+    if (out_dtype == EMU_OUT_E5M2 && x_fmt == EMU_FP8_E4M3FN && w_fmt == EMU_FP8_E4M3FN)
+        return fail(EMU_ERR_REJECTED, "e4m3fn x e4m3fn -> e5m2 is rejected (as cuBLASLt does)");
     if (ldo < N) return fail(EMU_ERR_INVALID_ARG, "ldo smaller than N");
     if (M == 0 || N == 0) return ok();
     if (!out || !scale_x || !scale_w) return fail(EMU_ERR_INVALID_ARG, "null output or scale pointer");
@@ -226,8 +232,8 @@ emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, co
         return fail(EMU_ERR_WORKSPACE, "workspace smaller than emu_workspace_bytes()");
     if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
         return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
-    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, scale_x, scale_w, out, kind, elem, ldo, fast_accum,
-               split_S, profile, workspace, workspace_bytes, stream);
+    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, scale_x, scale_w, scale_result, out, kind, elem, ldo,
+               fast_accum, split_S, profile, workspace, workspace_bytes, stream);
 }
 
 emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
@@ -247,8 +253,8 @@ emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, c
     if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
         return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
     // The scale pointers are not read for the accumulator.
-    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, nullptr, nullptr, acc, emu::OUT_ACC_F32, 4, ldacc,
-               fast_accum, split_S, profile, workspace, workspace_bytes, stream);
+    return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, nullptr, nullptr, nullptr, acc, emu::OUT_ACC_F32, 4,
+               ldacc, fast_accum, split_S, profile, workspace, workspace_bytes, stream);
 }
 
 const char *emu_status_string(emu_status status)
@@ -278,5 +284,7 @@ uint32_t emu_host_mul_f32(uint32_t a, uint32_t b) { return emu::mul_f32(a, b); }
 uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha) { return emu::canon_f32(emu::epilogue_f32(acc, alpha)); }
 uint16_t emu_host_f32_to_bf16(uint32_t f) { return emu::f32_to_bf16(f); }
 uint16_t emu_host_f32_to_f16(uint32_t f) { return emu::f32_to_f16(f); }
+uint8_t emu_host_f32_to_e4m3fn(uint32_t f) { return emu::f32_to_fp8_sat<true>(f); }
+uint8_t emu_host_f32_to_e5m2(uint32_t f) { return emu::f32_to_fp8_sat<false>(f); }
 
 }  // extern "C"

@@ -12,6 +12,8 @@ enum OutKind : int {
     OUT_BF16 = 1,     // epilogue, bf16
     OUT_F16 = 2,      // epilogue, binary16
     OUT_F32 = 3,      // epilogue, binary32
+    OUT_E4M3 = 4,     // epilogue, times scale_result, e4m3fn with saturation
+    OUT_E5M2 = 5,     // epilogue, times scale_result, e5m2 with saturation
 };
 
 struct MainParams {
@@ -34,6 +36,7 @@ struct MainParams {
     int64_t ldo;
     int64_t split_stride;  // elements between consecutive splits' partials in `out` (S > 1)
     const float *scale_x, *scale_w;
+    const float *scale_result;  // FP8 outputs only; null means 1
 };
 
 struct CombineParams {
@@ -44,6 +47,7 @@ struct CombineParams {
     void *out;
     int64_t ldo;
     const float *scale_x, *scale_w;
+    const float *scale_result;
 };
 
 // Tile configurations of the main kernel: rows x cols per workgroup; per

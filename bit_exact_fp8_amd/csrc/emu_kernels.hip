@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "emu_internal.h"
+#include "emu_output.h"
 #include "fp_round.h"
 
 namespace emu {
@@ -47,20 +48,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
         }
         acc = pend[L];
     }
-    const uint32_t a = __float_as_uint(acc);
-    if (p.out_kind == OUT_ACC_F32) {
-        reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(a);
-        return;
+    uint32_t alpha = 0, sr = 0x3F800000u;
+    if (p.out_kind != OUT_ACC_F32) {
+        alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
+        sr = scale_result_bits(p.scale_result);
     }
-    const uint32_t alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
-    const uint32_t y = epilogue_f32(a, alpha);
-    if (p.out_kind == OUT_BF16)
-        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_bf16(y);
-    else if (p.out_kind == OUT_F16)
-        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_f16(y);
-    else
-        reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(y);
+    store_epilogue(p.out_kind, p.out, m * p.ldo + n, __float_as_uint(acc), alpha, sr);
 }
+
 }  // namespace
 
 TileShape tile_shape(int cfg)

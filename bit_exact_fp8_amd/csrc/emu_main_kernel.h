@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include "emu_internal.h"
+#include "emu_output.h"
 #include "fp_round.h"
 
 namespace emu {
@@ -455,20 +456,14 @@ __device__ uint32_t special_acc(const uint8_t *xr, const uint8_t *wr, const Spli
 }
 
 __device__ __forceinline__ void store_output(const MainParams &p, int64_t m, int64_t n, uint32_t acc,
-                                             uint32_t alpha, int split)
+                                             uint32_t alpha, uint32_t sr, int split)
 {
-    if (p.out_kind == OUT_ACC_F32) {
+    if (p.out_kind == OUT_ACC_F32) {  // the accumulator, or this split's partial
         float *o = reinterpret_cast<float *>(p.out) + split * p.split_stride;
         reinterpret_cast<uint32_t *>(o)[m * p.ldo + n] = canon_f32(acc);
         return;
     }
-    const uint32_t y = epilogue_f32(acc, alpha);
-    if (p.out_kind == OUT_BF16)
-        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_bf16(y);
-    else if (p.out_kind == OUT_F16)
-        reinterpret_cast<uint16_t *>(p.out)[m * p.ldo + n] = f32_to_f16(y);
-    else
-        reinterpret_cast<uint32_t *>(p.out)[m * p.ldo + n] = canon_f32(y);
+    store_epilogue(p.out_kind, p.out, m * p.ldo + n, acc, alpha, sr);
 }
 
 // ---- the main kernel ---------------------------------------------------------
@@ -814,8 +809,11 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     }
     __syncthreads();
 
-    uint32_t alpha = 0;  // the scales are read only when the epilogue runs here
-    if (p.out_kind != OUT_ACC_F32) alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
+    uint32_t alpha = 0, sr = 0x3F800000u;  // the scales are read only when the epilogue runs here
+    if (p.out_kind != OUT_ACC_F32) {
+        alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
+        sr = scale_result_bits(p.scale_result);
+    }
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -825,7 +823,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             if (m >= p.M || n >= p.N || lane_g != 0) continue;
             uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
             if (flags[rm] | flags[BM + rn]) a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq);
-            store_output(p, m, n, a, alpha, split);
+            store_output(p, m, n, a, alpha, sr, split);
         }
 }
 

@@ -7,7 +7,8 @@
 // so the result never depends on the GPU's floating-point mode register
 // (rounding mode, denormal flushing) or on how the compiler treats float
 // code.  Round to nearest, ties to even; subnormals kept; overflow to
-// infinity; NaN results canonical (0x7FFFFFFF, 0x7FFF).
+// infinity (FP8 outputs: saturation); NaN results canonical (0x7FFFFFFF,
+// 0x7FFF, 0x7F).
 #pragma once
 
 #include <stdint.h>
@@ -121,6 +122,40 @@ EMU_HD uint16_t f32_to_f16(uint32_t f)
     const uint32_t half = 1u << (shift - 1);
     if (rem > half || (rem == half && (h & 1u))) h += 1;
     return (uint16_t)(s | h);
+}
+
+// binary32 -> FP8 (E4: e4m3fn, else e5m2) with saturation (validation page,
+// scope table row "Epilogue" and claims table: FP8 outputs saturate to the
+// format's largest finite value): |f| at or above 448 (e4m3fn) / 57344
+// (e5m2), infinities included, gives the signed largest finite value; other
+// values round to nearest even, subnormals kept, the sign of zero kept; NaN
+// gives 0x7F.
+template <bool E4>
+EMU_HD uint8_t f32_to_fp8_sat(uint32_t f)
+{
+    constexpr int MB = E4 ? 3 : 2;                             // mantissa bits
+    constexpr int BIAS = E4 ? 7 : 15;
+    constexpr int EMIN = 1 - BIAS;                             // -6, -14
+    constexpr uint32_t MAXF = E4 ? 0x43E00000u : 0x47600000u;  // 448.0f, 57344.0f
+    constexpr uint32_t MAXC = E4 ? 0x7Eu : 0x7Bu;
+    const uint32_t s = (f >> 24) & 0x80u;
+    const uint32_t a = f & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;
+    if (a >= MAXF) return (uint8_t)(s | MAXC);
+    if (a < 0x00800000u) return (uint8_t)s;  // binary32 subnormal: far below the FP8 subnormals
+    const int e = (int)(a >> 23) - 127;
+    const uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;        // value = sig * 2^(e - 23)
+    // quantum 2^((e < EMIN ? EMIN : e) - MB): drop `shift` low bits of sig
+    const int shift = 23 - MB + (e < EMIN ? EMIN - e : 0);
+    if (shift >= 25) return (uint8_t)s;                      // below half the smallest subnormal
+    uint32_t q = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1;
+    // subnormal: the code is q (q = 2^MB is the smallest normal's code);
+    // normal: a rounding carry moves into the exponent field by itself
+    const uint32_t code = (e < EMIN) ? q : ((uint32_t)(e + BIAS) << MB) + q - (1u << MB);
+    return (uint8_t)(s | code);
 }
 
 }  // namespace emu

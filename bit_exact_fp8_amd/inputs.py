@@ -31,7 +31,8 @@ import torch
 FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 FP8_MAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
 MANTISSA_BITS = {"e4m3fn": 3, "e5m2": 2}
-OUT_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+OUT_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32,
+              "e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
 @dataclass(frozen=True)

@@ -22,9 +22,14 @@
  *    give +0), and adds the partials serially, p0 + p1 + ... in binary32.
  *  - the epilogue is alpha = RN32(scale_x * scale_w), y32 = RN32(acc*alpha+(+0))
  *    (an exactly zero product gives +0), then round-to-nearest-even to the
- *    output type; subnormals are kept everywhere.
+ *    output type; subnormals are kept everywhere.  FP8 outputs first take
+ *    y' = RN32(y32 * scale_result), a plain binary32 multiplication, then
+ *    saturate: |y'| at or above the format's largest finite value (448 for
+ *    e4m3fn, 57344 for e5m2), infinities included, becomes that value
+ *    (validation page, scope table row "Epilogue" and claims table).
  *  - a NaN code anywhere in row m of x or row n of w makes output (m, n) the
- *    canonical NaN (0x7FFFFFFF for fp32, 0x7FFF for bf16/fp16).  E5M2
+ *    canonical NaN (0x7FFFFFFF for fp32, 0x7FFF for bf16/fp16, 0x7F for FP8;
+ *    the bit patterns are a reading: the pages say "canonical" only).  E5M2
  *    infinities follow IEEE: Inf*0 or infinite products of both signs give
  *    NaN, otherwise the signed infinity.
  *
@@ -33,7 +38,8 @@
  *   w   [N, K] row-major FP8 codes, leading dimension ldw (this is torch's
  *       mat2 = w.t(), a [K, N] column-major matrix);
  *   out [M, N] row-major, leading dimension ldo (elements >= N);
- *   scale_x, scale_w: one binary32 value each, read on the device.
+ *   scale_x, scale_w (and scale_result): one binary32 value each, read on
+ *       the device.
  *
  * Ordering and ownership: every call only enqueues kernels on `stream` and
  * returns; it never synchronises and never allocates device memory.  The
@@ -55,7 +61,7 @@
 extern "C" {
 #endif
 
-#define EMU_ABI_VERSION 1
+#define EMU_ABI_VERSION 2
 
 #if defined(EMU_BUILDING_LIBRARY)
 #define EMU_API __attribute__((visibility("default")))
@@ -66,19 +72,21 @@ extern "C" {
 typedef enum {
     EMU_OK = 0,
     EMU_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad leading dimension, unknown enum, split_S < 1 */
-    EMU_ERR_REJECTED = 2,    /* a call torch 2.7.1 / cuBLASLt would reject (limitations page, features table):
-                                e5m2 x e5m2, K or N not a multiple of 16, x / w / out not 16-byte aligned,
+    EMU_ERR_REJECTED = 2,    /* a call torch 2.7.1 / cuBLASLt would reject (limitations page, features table;
+                                validation page, claims table): e5m2 x e5m2, e4m3fn x e4m3fn -> e5m2,
+                                K or N not a multiple of 16, x / w / out not 16-byte aligned,
                                 ldx or ldw not a multiple of 16 */
-    EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: FP8 outputs, split_S above 65535,
-                                M or N above 2^31-1 */
+    EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: split_S above 65535, M or N above 2^31-1,
+                                scale_result with a non-FP8 output */
     EMU_ERR_WORKSPACE = 4,   /* workspace_bytes < emu_workspace_bytes(...) */
     EMU_ERR_DEVICE = 5       /* a HIP launch or runtime error */
 } emu_status;
 
 typedef enum { EMU_FP8_E4M3FN = 0, EMU_FP8_E5M2 = 1 } emu_fp8_format;
 
-/* 3 and 4 are reserved for FP8 outputs (e4m3fn, e5m2), which this library
- * does not build: they return EMU_ERR_UNSUPPORTED. */
+/* Output types.  FP8 outputs (e4m3fn, e5m2) are one byte per element, with
+ * scale_result and saturation; e4m3fn x e4m3fn inputs cannot produce e5m2
+ * (rejected, as cuBLASLt does on both reference platforms). */
 typedef enum {
     EMU_OUT_BF16 = 0,
     EMU_OUT_FP16 = 1,
@@ -114,6 +122,10 @@ typedef enum {
  * y = (x @ w.T) * scale_x * scale_w (torch._scaled_mm semantics with
  * tensor-wise scales; user guide section 3).
  *
+ * scale_result: NULL, or (FP8 outputs only) a device pointer to one binary32
+ * value; NULL means no scale_result (the same bits as 1.0).  A non-NULL
+ * scale_result with a bf16 / fp16 / fp32 output returns EMU_ERR_UNSUPPORTED.
+ *
  * M >= 0 (any value), N >= 0 and K >= 0 multiples of 16.  M = 0 or N = 0
  * returns EMU_OK without enqueuing anything; K = 0 writes +0 everywhere.
  * workspace: device memory of at least emu_workspace_bytes(M, N, K, split_S,
@@ -123,7 +135,7 @@ typedef enum {
 EMU_API emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
                          const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
                          int64_t M, int64_t N, int64_t K,
-                         const float *scale_x, const float *scale_w,
+                         const float *scale_x, const float *scale_w, const float *scale_result,
                          void *out, emu_out_dtype out_dtype, int64_t ldo,
                          int fast_accum, int split_S, emu_profile profile,
                          void *workspace, size_t workspace_bytes, void *stream);
@@ -177,11 +189,16 @@ EMU_API int emu_debug_force_tile(int cfg);
  *   emu_host_epilogue_f32: RN32(acc * alpha + (+0)); NaN results 0x7FFFFFFF.
  *   emu_host_f32_to_bf16 / emu_host_f32_to_f16: round to nearest even,
  *       subnormals kept, overflow to infinity, NaN -> 0x7FFF.
+ *   emu_host_f32_to_e4m3fn / emu_host_f32_to_e5m2: round to nearest even,
+ *       subnormals kept, saturation to +-448 / +-57344 (infinities
+ *       included), NaN -> 0x7F.
  */
 EMU_API uint32_t emu_host_mul_f32(uint32_t a, uint32_t b);
 EMU_API uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha);
 EMU_API uint16_t emu_host_f32_to_bf16(uint32_t f);
 EMU_API uint16_t emu_host_f32_to_f16(uint32_t f);
+EMU_API uint8_t emu_host_f32_to_e4m3fn(uint32_t f);
+EMU_API uint8_t emu_host_f32_to_e5m2(uint32_t f);
 
 #ifdef __cplusplus
 }

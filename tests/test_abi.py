@@ -44,7 +44,10 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert api.abi_version() == 1
+    """The library reports the EMU_ABI_VERSION of the header it was built with."""
+    hdr = open(os.path.join(ROOT, "include", "emu_fp8gemm.h")).read()
+    want = int(hdr.split("#define EMU_ABI_VERSION")[1].split()[0])
+    assert api.abi_version() == want == 2
 
 
 def test_status_strings(lib):
@@ -58,11 +61,11 @@ def test_workspace_bytes():
     assert api._lib().emu_workspace_bytes(-1, 16, 16, 2, 1, 0) == 0
 
 
-def call(lib, x=16, xf=0, ldx=32, w=16, wf=0, ldw=32, M=4, N=16, K=32, sx=4, sw=4, out=16,
+def call(lib, x=16, xf=0, ldx=32, w=16, wf=0, ldw=32, M=4, N=16, K=32, sx=4, sw=4, sr=None, out=16,
          od=0, ldo=16, fast=1, S=1, prof=0, ws=0, wsb=0):
     """emu_scaled_mm with fake (never dereferenced) device addresses: every
     case here must fail its host-side checks before any launch."""
-    return lib.emu_scaled_mm(x, xf, ldx, w, wf, ldw, M, N, K, sx, sw, out, od, ldo, fast, S, prof, ws,
+    return lib.emu_scaled_mm(x, xf, ldx, w, wf, ldw, M, N, K, sx, sw, sr, out, od, ldo, fast, S, prof, ws,
                              wsb, None)
 
 
@@ -83,10 +86,14 @@ CASES = [
     (dict(x=24), api.EMU_ERR_REJECTED),          # misaligned storage
     (dict(out=24), api.EMU_ERR_REJECTED),
     (dict(ldx=40), api.EMU_ERR_REJECTED),
-    (dict(od=3), api.EMU_ERR_UNSUPPORTED),       # FP8 outputs
-    (dict(od=4), api.EMU_ERR_UNSUPPORTED),
+    (dict(od=4), api.EMU_ERR_REJECTED),          # e4m3fn x e4m3fn -> e5m2
+    (dict(od=0, sr=4), api.EMU_ERR_UNSUPPORTED), # scale_result with a bf16 output
+    (dict(od=2, sr=4), api.EMU_ERR_UNSUPPORTED),
+    (dict(od=5), api.EMU_ERR_INVALID_ARG),       # unknown output type
+    (dict(od=3, out=8), api.EMU_ERR_REJECTED),   # misaligned FP8 output
     (dict(prof=3), api.EMU_ERR_INVALID_ARG),     # unknown profile
     (dict(S=2), api.EMU_ERR_WORKSPACE),
+    (dict(od=3, sr=4, S=2), api.EMU_ERR_WORKSPACE),  # FP8 output with scale_result passes the other checks
     (dict(S=2, ws=16, wsb=100), api.EMU_ERR_WORKSPACE),
 ]
 
@@ -168,6 +175,32 @@ def test_host_bf16_and_f16_rounding(lib):
     got_h = np.array([lib.emu_host_f32_to_f16(int(v)) for v in f], dtype=np.uint16)
     assert np.array_equal(got_bf, want_bf)
     assert np.array_equal(got_h, want_h)
+
+
+def test_host_fp8_saturating_rounding(lib):
+    """binary32 -> e4m3fn / e5m2 with saturation: numpy's clip to the largest
+    finite value (infinities included), then torch's round-to-nearest-even
+    FP8 conversion; NaN -> 0x7F.  Random patterns, every binary32 exponent,
+    and the exact FP8 ties of both formats."""
+    rng = np.random.default_rng(2)
+    ties = np.concatenate([
+        (_u32(20000, rng) & np.uint32(0x80000000)) | ((rng.integers(100, 140, 20000) << 23).astype(np.uint32))
+        | (_u32(20000, rng) & np.uint32(0x00700000)) | np.uint32(0x00080000),
+        (_u32(20000, rng) & np.uint32(0x80000000)) | ((rng.integers(90, 145, 20000) << 23).astype(np.uint32))
+        | (_u32(20000, rng) & np.uint32(0x00600000)) | np.uint32(0x00100000)])
+    f = np.concatenate([_u32(100000, rng), _edge_patterns(), ties])
+    fl = f.view(np.float32)
+    for name, dt, mx in (("emu_host_f32_to_e4m3fn", torch.float8_e4m3fn, 448.0),
+                         ("emu_host_f32_to_e5m2", torch.float8_e5m2, 57344.0)):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_uint8
+        fn.argtypes = [ctypes.c_uint32]
+        clipped = np.clip(fl, np.float32(-mx), np.float32(mx))
+        want = torch.from_numpy(clipped.copy()).to(dt).view(torch.uint8).numpy()
+        want = np.where(np.isnan(fl), np.uint8(0x7F), want)
+        got = np.array([fn(int(v)) for v in f], dtype=np.uint8)
+        bad = np.argwhere(got != want)
+        assert len(bad) == 0, (name, [(hex(int(f[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:5, 0]])
 
 
 def test_host_mul_and_epilogue(lib):

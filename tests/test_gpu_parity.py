@@ -44,30 +44,34 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     t = t.cpu()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy().astype(np.uint32)
     return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
 
 
 def gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, stream=None, prefill=None,
-            profile="hopper"):
+            profile="hopper", sr=None):
     xd = x.to(dev).view(FP8_DTYPES[xfmt])
     wd = w.to(dev).view(FP8_DTYPES[wfmt])
     sxd = torch.tensor([sx], dtype=torch.float32, device=dev)
     swd = torch.tensor([sw], dtype=torch.float32, device=dev)
+    srd = None if sr is None else torch.tensor([sr], dtype=torch.float32, device=dev)
     o = None
     if prefill is not None:
         o = torch.empty((x.shape[0], w.shape[0]), dtype=OUT_DTYPES[out], device=dev)
         o.view(torch.uint8).fill_(prefill)
     with torch.cuda.stream(stream or torch.cuda.current_stream(dev)):
         y = api.scaled_mm(xd, wd.t(), sxd, swd, out_dtype=OUT_DTYPES[out], use_fast_accum=fast,
-                          split_S=S, profile=profile, out=o)
+                          split_S=S, profile=profile, out=o, scale_result=srd)
         acc = api.accumulate(xd, wd, use_fast_accum=fast, split_S=S, profile=profile)
     torch.cuda.synchronize(dev)
     return bits_of(y), bits_of(acc)
 
 
-def oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, profile="hopper"):
+def oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out="bf16", fast=True, S=1, profile="hopper", sr=None):
     return orc.scaled_mm(x.numpy(), xfmt, w.numpy(), wfmt, scale_bits(sx), scale_bits(sw), out, fast, S,
-                         profile=profile, threads=THREADS)
+                         profile=profile, threads=THREADS,
+                         sr_bits=oracle.ONE if sr is None else scale_bits(sr))
 
 
 def assert_same(got, want, what):
@@ -79,11 +83,11 @@ def assert_same(got, want, what):
                              f"gpu {int(got[i]):#x} oracle {int(want[i]):#x}")
 
 
-def check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, what, profile="hopper"):
+def check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, what, profile="hopper", sr=None):
     note(f"[gpu] {what}: M={x.shape[0]} N={w.shape[0]} K={x.shape[1]} {xfmt}x{wfmt} "
-         f"fast={fast} S={S} out={out} profile={profile}")
-    y, acc = gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile)
-    acc_o, y_o = oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile)
+         f"fast={fast} S={S} out={out} profile={profile} scale_result={sr}")
+    y, acc = gpu_run(dev, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile, sr=sr)
+    acc_o, y_o = oracle_run(orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, profile=profile, sr=sr)
     assert_same(acc, acc_o, what + " accumulator")
     assert_same(y, y_o, what + " output")
 
@@ -131,6 +135,10 @@ def test_every_code_pair(dev, orc, xfmt, wfmt):
     w[:, 3] = codes
     for out in ("bf16", "fp16", "fp32"):
         check(dev, orc, x, xfmt, w, wfmt, 1 / 3, 0.1, out, True, 1, f"code pairs {xfmt}x{wfmt}")
+    for out, sr in (("e4m3fn", None), ("e4m3fn", 9.6), ("e5m2", -0.37)):
+        if out == "e5m2" and xfmt == wfmt == "e4m3fn":
+            continue  # rejected combination
+        check(dev, orc, x, xfmt, w, wfmt, 1 / 3, 0.1, out, True, 1, f"code pairs {xfmt}x{wfmt}", sr=sr)
 
 
 # ---- edge-case sweep --------------------------------------------------------------
@@ -196,6 +204,44 @@ def test_every_tile_config(dev, orc, cfg, shape, profile):
                   f"tile {api.TILE_CONFIGS[cfg]} {shape}", profile=profile)
     finally:
         api.force_tile(prev)
+
+
+# ---- FP8 outputs ------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(16))
+def test_fp8_outputs(dev, orc, seed):
+    """FP8 outputs (scale_result, saturation, subnormals, NaN) over the edge
+    cases: ragged sizes, splits (the combine kernel's store), both profiles,
+    scale_result absent, fractional, negative, tiny or huge."""
+    x, xfmt, w, wfmt, sx, sw, _, fast, S = _edge_case(2000 + seed)
+    out = "e4m3fn" if (seed % 2 == 0 or xfmt == wfmt) else "e5m2"
+    sr = [None, 0.3, -7.5, 2.0 ** -10, 3.0e5, 1.0][seed % 6]
+    profile = ("hopper", "ada-pairwise")[seed % 2]
+    check(dev, orc, x, xfmt, w, wfmt, sx, sw, out, fast, S, f"fp8 output {seed}", profile=profile, sr=sr)
+
+
+def test_fp8_output_workload(dev, orc):
+    """The user guide's example shape with an e4m3fn output (torch's default
+    out_dtype for e4m3fn inputs) and a scale_result that saturates part of it."""
+    wl = WORKLOADS["proj_64x5760x1920"]
+    x, w = make_operands(wl, 0)
+    check(dev, orc, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, "e4m3fn", wl.fast, 1,
+          "proj e4m3fn output", sr=0.75)
+
+
+def test_fp8_rejections(dev):
+    """e4m3fn x e4m3fn -> e5m2 is rejected; scale_result needs an FP8 output."""
+    x, w = make_operands(WORKLOADS["tiny"], 0)
+    xd = x.to(dev).view(torch.float8_e4m3fn)
+    wd = w.to(dev).view(torch.float8_e4m3fn)
+    one = torch.ones(1, device=dev)
+    with pytest.raises(api.EmuError) as e:
+        api.scaled_mm(xd, wd.t(), one, one, out_dtype=torch.float8_e5m2)
+    assert e.value.status == api.EMU_ERR_REJECTED
+    with pytest.raises(api.EmuError) as e:
+        api.scaled_mm(xd, wd.t(), one, one, out_dtype=torch.bfloat16, scale_result=one)
+    assert e.value.status == api.EMU_ERR_UNSUPPORTED
+    y = api.scaled_mm(xd, wd.t(), one, one)  # out_dtype defaults to the input dtype
+    assert y.dtype == torch.float8_e4m3fn
 
 
 # ---- the RTX 4060 (ada) profiles ------------------------------------------------
