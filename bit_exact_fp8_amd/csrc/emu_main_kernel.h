@@ -466,6 +466,30 @@ __device__ __forceinline__ void store_output(const MainParams &p, int64_t m, int
     store_epilogue(p.out_kind, p.out, m * p.ldo + n, acc, alpha, sr);
 }
 
+// XCD-aware tile order.  The workgroups of a launch are dealt round-robin to
+// the 8 XCDs (workgroup id mod 8), each with its own L2.  When the tile
+// count allows, ids are renumbered so that XCD j takes the j-th eighth of
+// the tiles, and the tiles are walked in groups of TILE_GROUP tile-rows,
+// column by column inside a group: the workgroups resident on one XCD then
+// cover a compact block of tile-rows and tile-columns and share their
+// operand rows in that XCD's L2.  A bijection on any grid.
+constexpr int TILE_GROUP = 8;
+
+__device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
+{
+    const int64_t nx = gridDim.x, ny = gridDim.y;
+    const int64_t T = nx * ny;
+    int64_t id = (int64_t)blockIdx.y * nx + blockIdx.x;
+    if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
+    const int64_t per_group = TILE_GROUP * nx;
+    const int64_t g = id / per_group;
+    const int64_t first = g * TILE_GROUP;
+    const int64_t rows = (ny - first < TILE_GROUP) ? ny - first : TILE_GROUP;
+    const int64_t r = id - g * per_group;
+    tile_m = (int)(first + r % rows);
+    tile_n = (int)(r / rows);
+}
+
 // ---- the main kernel ---------------------------------------------------------
 // Workgroup tile BM x BN outputs of one split; thread tile RM x RN with rows
 // tm + i*TM and columns tn + j*TN (interleaved, so that the lanes of a wave
@@ -530,7 +554,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         for (int i = t; i < BM * PW_ROW; i += NT) reinterpret_cast<uint4 *>(xp)[i] = make_uint4(0, 0, 0, 0);
         for (int i = t; i < BN * PW_ROW; i += NT) reinterpret_cast<uint4 *>(wp)[i] = make_uint4(0, 0, 0, 0);
     }
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    int tile_m, tile_n;
+    tile_order(tile_m, tile_n);
+    const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
     const int split = blockIdx.z;
     const SplitSeq sq = split_seq(p, split);
     const int64_t tile_mask = (int64_t(1) << p.tile_shift) - 1;
