@@ -73,7 +73,8 @@ def abi_version() -> int:
     return _lib().emu_abi_version()
 
 
-TILE_CONFIGS = ("64x128", "64x64", "32x64", "32x32", "16x16_g2", "16x16_g4", "64x64_mx", "64x128_mx")
+TILE_CONFIGS = ("64x128", "64x64", "32x64", "32x32", "16x16_g2", "16x16_g4", "64x64_mx", "64x128_mx",
+                "16x8_g4")
 
 
 def force_tile(cfg: int) -> int:

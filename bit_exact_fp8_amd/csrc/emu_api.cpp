@@ -69,8 +69,9 @@ std::atomic<int> g_forced_tile{-1};
 
 // Pick the tile configuration with the best expected throughput: its
 // measured steady-state efficiency on MI355X (fraction of the integer-VALU
-// roofline once the GPU holds at least two waves per SIMD) scaled down by
-// how far the launch falls short of 2 waves on each of the 1,024 SIMDs.
+// roofline on a full machine) scaled down by how far the launch falls short
+// of 2 waves on each of the 1,024 SIMDs and of one workgroup on each of the
+// 256 CUs.
 int choose_tile(int64_t M, int64_t N, int S)
 {
     const int forced = g_forced_tile.load(std::memory_order_relaxed);
@@ -81,14 +82,14 @@ int choose_tile(int64_t M, int64_t N, int S)
     };
     const Cand cands[] = {{emu::TILE_64x64_MX, 1.08}, {emu::TILE_64x128_MX, 0.98}, {emu::TILE_64x64, 0.90},
                           {emu::TILE_64x128, 0.87}, {emu::TILE_32x64, 0.60}, {emu::TILE_32x32, 0.60},
-                          {emu::TILE_16x16_G2, 0.27}, {emu::TILE_16x16_G4, 0.15}};
-    int best = emu::TILE_16x16_G4;
+                          {emu::TILE_16x16_G2, 0.30}, {emu::TILE_16x16_G4, 0.24}, {emu::TILE_16x8_G4, 0.24}};
+    int best = emu::TILE_16x8_G4;
     double best_est = -1.0;
     for (const Cand &c : cands) {
         const emu::TileShape t = emu::tile_shape(c.cfg);
-        const double waves = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn) * S *
-                             (t.threads / 64);
-        const double est = c.eff * (waves >= 2048.0 ? 1.0 : waves / 2048.0);
+        const double wgs = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn) * S;
+        const double waves = wgs * (t.threads / 64);
+        const double est = c.eff * (waves >= 2048.0 ? 1.0 : waves / 2048.0) * (wgs >= 256.0 ? 1.0 : wgs / 256.0);
         if (est > best_est) {
             best_est = est;
             best = c.cfg;

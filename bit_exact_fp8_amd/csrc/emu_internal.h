@@ -52,7 +52,8 @@ struct CombineParams {
 
 // Tile configurations of the main kernel: rows x cols per workgroup; per
 // thread 4x8, 4x4, 2x4, 2x2 outputs, or one output chain shared by 2 or 4
-// lanes (G2, G4); MX: block exponent maxima on the matrix cores.
+// lanes (G2, G4; these stage 8 K-blocks per barrier); MX: block exponent
+// maxima on the matrix cores.
 enum TileConfig : int {
     TILE_64x128 = 0,
     TILE_64x64 = 1,
@@ -62,7 +63,8 @@ enum TileConfig : int {
     TILE_16x16_G4 = 5,
     TILE_64x64_MX = 6,
     TILE_64x128_MX = 7,
-    TILE_COUNT = 8
+    TILE_16x8_G4 = 8,
+    TILE_COUNT = 9
 };
 
 struct TileShape {

@@ -69,6 +69,7 @@ TileShape tile_shape(int cfg)
     case TILE_16x16_G4: return {16, 16, 1024};
     case TILE_64x64_MX: return {64, 64, 256};
     case TILE_64x128_MX: return {64, 128, 256};
+    case TILE_16x8_G4: return {16, 8, 512};
     default: return {64, 128, 256};
     }
 }

@@ -514,7 +514,7 @@ struct WavesPerSimd {
 // wave per 16 rows: the wave's 16 x (16*RN) output tile is RN 16x16
 // matrix-instruction tiles, and lane l owns rows 4*(l/16) + i and columns
 // l%16 + 16*j, the layout of v_mfma_f32_16x16x16_bf16's result.
-template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST, bool MX, int BLK>
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST, bool MX, int BLK, int SS>
 __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
@@ -523,7 +523,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                   "matrix-instruction exponents need 16-row waves with 4x RN thread tiles");
     constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per stage: two per row
-    constexpr int CPT = (NCHUNK + NT - 1) / NT;
+    constexpr int CPT = (NCHUNK * SS + NT - 1) / NT;
     constexpr int NBS = KB / BLK;          // blocks per stage
     constexpr int QPB = BLK / 8;           // quarter-blocks (8 products) per block
     constexpr int WPB = BLK / 2;           // exponent-plane words per block
@@ -531,13 +531,16 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr int WU = (WPL >= 4) ? 4 : 2; // words per exponent-plane read
     constexpr int K4PL = BLK / 4 / G;      // groups of 4 products per lane and block
     static_assert(WPL % WU == 0 && K4PL >= 1, "block slice per lane");
+    static_assert(SS >= 1 && (!MX || SS == 1), "stages per barrier: matrix-core exponents use one");
+    constexpr int XA = BM * A_STRIDE, XP = BM * P_STRIDE, WA = BN * A_STRIDE, WP = BN * P_STRIDE;
 
-    __shared__ __attribute__((aligned(16))) float xa[BM * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t xe[MX ? 4 : BM * P_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t xs[BM * P_STRIDE];
-    __shared__ __attribute__((aligned(16))) float wa[BN * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t we[MX ? 4 : BN * P_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint32_t wsg[BN * P_STRIDE];
+    // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
+    __shared__ __attribute__((aligned(16))) float xa_all[SS * XA];
+    __shared__ __attribute__((aligned(16))) uint32_t xe_all[MX ? 4 : SS * XP];
+    __shared__ __attribute__((aligned(16))) uint32_t xs_all[SS * XP];
+    __shared__ __attribute__((aligned(16))) float wa_all[SS * WA];
+    __shared__ __attribute__((aligned(16))) uint32_t we_all[MX ? 4 : SS * WP];
+    __shared__ __attribute__((aligned(16))) uint32_t wsg_all[SS * WP];
     __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
     __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
     __shared__ uint32_t flags[BM + BN];
@@ -569,25 +572,33 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
     for (int q = 0; q < CPT; ++q) myflag[q] = 0;
 
-    // Stage at sequence position pos (a multiple of 32, inside one k-tile):
-    // k from sq.k_of(pos), up to the end of that tile or of K; codes past it
-    // load as zeros (zero products: neutral in every block).
+    // Stages at sequence positions pos, pos + 32, ..., pos + 32*(SS-1) (each a
+    // multiple of 32 inside one k-tile): chunk idx = t + q*NT is stage
+    // idx / NCHUNK, row (idx % NCHUNK) >> 1 (x rows first), half idx & 1.
+    // k runs from sq.k_of(stage position) up to the end of that tile or of
+    // K; codes past it, and stages past the k-list, load as zeros (zero
+    // products: neutral in every block).
     auto load_block = [&](int64_t pos) {
-        const int64_t kb = sq.k_of(pos);
-        const int64_t tile_end = kb - (pos & tile_mask) + tile_mask + 1;
-        const int64_t lim = tile_end < p.K ? tile_end : p.K;
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
             raw[q] = make_uint4(0, 0, 0, 0);
-            if (idx < NCHUNK) {
-                const int r = idx >> 1, half = idx & 1;
-                const int64_t k = kb + 16 * half;
-                if (k < lim) {
-                    if (r < BM) {
-                        if (m0 + r < p.M) raw[q] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + k);
-                    } else if (n0 + (r - BM) < p.N) {
-                        raw[q] = *reinterpret_cast<const uint4 *>(p.w + (n0 + r - BM) * p.ldw + k);
+            if (idx < NCHUNK * SS) {
+                const int st = idx / NCHUNK, c = idx % NCHUNK;
+                const int r = c >> 1, half = c & 1;
+                const int64_t sp = pos + (int64_t)st * KB;
+                if (sp < sq.len) {
+                    const int64_t kb = sq.k_of(sp);
+                    const int64_t tile_end = kb - (sp & tile_mask) + tile_mask + 1;
+                    const int64_t lim = tile_end < p.K ? tile_end : p.K;
+                    const int64_t k = kb + 16 * half;
+                    if (k < lim) {
+                        if (r < BM) {
+                            if (m0 + r < p.M)
+                                raw[q] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + k);
+                        } else if (n0 + (r - BM) < p.N) {
+                            raw[q] = *reinterpret_cast<const uint4 *>(p.w + (n0 + r - BM) * p.ldw + k);
+                        }
                     }
                 }
             }
@@ -610,16 +621,19 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     }
 
     if (sq.len > 0) load_block(0);
-    for (int64_t pos = 0; pos < sq.len; pos += KB) {
-        __syncthreads();  // previous stage's readers are done with the LDS planes
+    for (int64_t pos = 0; pos < sq.len; pos += (int64_t)KB * SS) {
+        __syncthreads();  // previous stages' readers are done with the LDS planes
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
-            if (idx < NCHUNK) {
-                const int r = idx >> 1, half = idx & 1;
+            if (idx < NCHUNK * SS) {
+                const int st = idx / NCHUNK, c = idx % NCHUNK;
+                const int r = c >> 1, half = c & 1;
                 if (r < BM) {
                     myflag[q] |= has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
                                  has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
+                    float *xa = xa_all + st * XA;
+                    uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XP;
                     if (MX)
                         decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
                                                        xs + r * P_STRIDE + 8 * half,
@@ -632,6 +646,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     const int rw = r - BM;
                     myflag[q] |= has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
                                  has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
+                    float *wa = wa_all + st * WA;
+                    uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WP;
                     if (MX)
                         decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
                                                        wsg + rw * P_STRIDE + 8 * half,
@@ -644,8 +660,16 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             }
         }
         __syncthreads();
-        if (pos + KB < sq.len) load_block(pos + KB);  // prefetch; latency hidden by the compute below
+        // prefetch the next stages; latency hidden by the compute below
+        if (pos + (int64_t)KB * SS < sq.len) load_block(pos + (int64_t)KB * SS);
 
+#pragma unroll 1
+        for (int st = 0; st < SS; ++st) {
+        const int64_t spos = pos + (int64_t)st * KB;
+        if (spos >= sq.len) break;  // uniform across the workgroup
+        const float *xa = xa_all + st * XA, *wa = wa_all + st * WA;
+        const uint32_t *xe = xe_all + (MX ? 0 : st * XP), *we = we_all + (MX ? 0 : st * WP);
+        const uint32_t *xs = xs_all + st * XP, *wsg = wsg_all + st * WP;
 #pragma unroll
         for (int hb = 0; hb < NBS; ++hb) {
             uint32_t Cb[RM][RN];
@@ -807,7 +831,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 
         // slow accumulation: add the chunk result every 128 positions of the
         // split's k-list, in order
-        if (!FAST && (((pos + KB) & (CHUNK - 1)) == 0 || pos + KB >= sq.len)) {
+        if (!FAST && (((spos + KB) & (CHUNK - 1)) == 0 || spos + KB >= sq.len)) {
             uint32_t dep = 0;
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -825,13 +849,14 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 }
             tok = mode_round_toward_zero_after(dep2);
         }
+        }  // stages
     }
 
     // rows holding NaN / Inf codes in this split's k-list
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
         const int idx = t + q * NT;
-        if (idx < NCHUNK && myflag[q]) atomicOr(&flags[idx >> 1], 1u);
+        if (idx < NCHUNK * SS && myflag[q]) atomicOr(&flags[(idx % NCHUNK) >> 1], 1u);
     }
     __syncthreads();
 
@@ -853,15 +878,16 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         }
 }
 
-template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool MX, int BLK>
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool MX, int BLK, int SS = 1>
 hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
 {
     constexpr int NT = (BM / RM) * (BN / RN) * G;
     dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, S);
     if (p.fast)
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true, MX, BLK>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true, MX, BLK, SS>), grid, dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false, MX, BLK>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false, MX, BLK, SS>), grid, dim3(NT), 0, stream,
+                           p);
     return hipGetLastError();
 }
 
@@ -873,10 +899,11 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_64x64: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, false, BLK>(p, S, stream);
     case TILE_32x64: return launch_cfg<XF, WF, 32, 64, 2, 4, 1, false, BLK>(p, S, stream);
     case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK>(p, S, stream);
-    case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2, false, BLK>(p, S, stream);
-    case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4, false, BLK>(p, S, stream);
+    case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2, false, BLK, 8>(p, S, stream);
+    case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4, false, BLK, 8>(p, S, stream);
     case TILE_64x64_MX: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_64x128_MX: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, S, stream);
+    case TILE_16x8_G4: return launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }

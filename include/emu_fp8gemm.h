@@ -172,9 +172,10 @@ EMU_API int emu_abi_version(void);
 /*
  * Testing and tuning: force the main kernel's tile configuration for every
  * later call in the process (cfg = -1 restores the automatic choice; valid
- * configurations are 0 .. 7: 64x128, 64x64, 32x64, 32x32 output tiles with
+ * configurations are 0 .. 8: 64x128, 64x64, 32x64, 32x32 output tiles with
  * one lane per output, 16x16 with 2 or 4 lanes per output, 64x64 and
- * 64x128 with the block exponent maxima on the matrix cores).  Results do not
+ * 64x128 with the block exponent maxima on the matrix cores, 16x8 with 4
+ * lanes per output).  Results do not
  * depend on the configuration.  Returns the previous setting, or -2 (and
  * changes nothing) for an invalid cfg.  Process-wide; not for concurrent use
  * with calls that expect the automatic choice.

@@ -225,3 +225,17 @@ def test_host_mul_and_epilogue(lib):
     got_epi = np.array([lib.emu_host_epilogue_f32(int(x), int(y)) for x, y in zip(a, b)], dtype=np.uint32)
     assert np.array_equal(got_mul, want_mul), np.argwhere(got_mul != want_mul)[:5]
     assert np.array_equal(got_epi, want_epi), np.argwhere(got_epi != want_epi)[:5]
+
+
+def test_force_tile_range(lib):
+    """Every configuration the binding names is accepted; the next index is
+    refused without changing the setting."""
+    prev = api.force_tile(-1)
+    try:
+        for cfg in range(len(api.TILE_CONFIGS)):
+            api.force_tile(cfg)
+        with pytest.raises(ValueError):
+            api.force_tile(len(api.TILE_CONFIGS))
+        assert api.force_tile(-1) == len(api.TILE_CONFIGS) - 1
+    finally:
+        api.force_tile(prev)

@@ -186,7 +186,7 @@ def test_large_tiles(dev, orc, fast, S):
 
 
 @pytest.mark.parametrize("profile", ["hopper", "ada-pairwise"])
-@pytest.mark.parametrize("cfg", range(8))
+@pytest.mark.parametrize("cfg", range(len(api.TILE_CONFIGS)))
 @pytest.mark.parametrize("shape", [(1, 16, 48), (37, 80, 400), (70, 144, 1040)])
 def test_every_tile_config(dev, orc, cfg, shape, profile):
     """Every tile configuration (including 2 and 4 lanes per output) gives the
