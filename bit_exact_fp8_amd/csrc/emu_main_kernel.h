@@ -370,12 +370,17 @@ __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve,
     }
 }
 
-// Any NaN (E4M3) or Inf/NaN (E5M2) code among four packed codes.
+// Row flags of four packed codes: bit 0 for any NaN or Inf code, bit 1 for
+// a NaN code (E4M3FN: magnitude 0x7F; E5M2: magnitude above 0x7C, Inf being
+// 0x7C).
 template <int FMT>
-__device__ __forceinline__ uint32_t has_special(uint32_t v)
+__device__ __forceinline__ uint32_t special_flags(uint32_t v)
 {
-    if (FMT == FMT_E4M3) return ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
-    return ((v & 0x7C7C7C7Cu) + 0x04040404u) & 0x80808080u;
+    const uint32_t mag = v & 0x7F7F7F7Fu;
+    if (FMT == FMT_E4M3) return (((mag + 0x01010101u) & 0x80808080u) != 0) ? 3u : 0u;
+    const uint32_t any = (mag + 0x04040404u) & 0x80808080u;  // magnitude >= 0x7C
+    const uint32_t nan = (mag + 0x03030303u) & 0x80808080u;  // magnitude >= 0x7D
+    return (any ? 1u : 0u) | (nan ? 2u : 0u);
 }
 
 template <int FMT>
@@ -429,11 +434,11 @@ __device__ __forceinline__ SplitSeq split_seq(const MainParams &p, int z)
     return q;
 }
 
-// The non-finite result of one output over a split's k-list: NaN if a NaN
-// code is in either row, if some k pairs an infinity with a zero, or if
-// infinite products of both signs occur; otherwise the signed infinity.
-// Only called for rows that hold a NaN or Inf code in that k-list, so the
-// result is never finite.
+// The non-finite result of one output over a split's k-list: NaN if some k
+// pairs an infinity with a zero or infinite products of both signs occur,
+// otherwise the signed infinity.  Called only when a row holds an E5M2
+// infinity (rows with a NaN code resolve to the canonical NaN without it),
+// so the result is never finite; it also honours NaN codes, for clarity.
 template <int XF, int WF>
 __device__ uint32_t special_acc(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq)
 {
@@ -630,8 +635,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 const int st = idx / NCHUNK, c = idx % NCHUNK;
                 const int r = c >> 1, half = c & 1;
                 if (r < BM) {
-                    myflag[q] |= has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
-                                 has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
+                    myflag[q] |= special_flags<XF>(raw[q].x) | special_flags<XF>(raw[q].y) |
+                                 special_flags<XF>(raw[q].z) | special_flags<XF>(raw[q].w);
                     float *xa = xa_all + st * XA;
                     uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XP;
                     if (MX)
@@ -644,8 +649,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                                                   xe + r * P_STRIDE + 8 * half, xs + r * P_STRIDE + 8 * half);
                 } else {
                     const int rw = r - BM;
-                    myflag[q] |= has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
-                                 has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
+                    myflag[q] |= special_flags<WF>(raw[q].x) | special_flags<WF>(raw[q].y) |
+                                 special_flags<WF>(raw[q].z) | special_flags<WF>(raw[q].w);
                     float *wa = wa_all + st * WA;
                     uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WP;
                     if (MX)
@@ -852,11 +857,11 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         }  // stages
     }
 
-    // rows holding NaN / Inf codes in this split's k-list
+    // rows holding NaN / Inf codes in this split's k-list (special_flags bits)
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
         const int idx = t + q * NT;
-        if (idx < NCHUNK * SS && myflag[q]) atomicOr(&flags[(idx % NCHUNK) >> 1], 1u);
+        if (idx < NCHUNK * SS && myflag[q]) atomicOr(&flags[(idx % NCHUNK) >> 1], myflag[q]);
     }
     __syncthreads();
 
@@ -873,7 +878,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             const int64_t m = m0 + rm, n = n0 + rn;
             if (m >= p.M || n >= p.N || lane_g != 0) continue;
             uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
-            if (flags[rm] | flags[BM + rn]) a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq);
+            const uint32_t f = flags[rm] | flags[BM + rn];
+            if (f & 2u) a = kCanonNan32;  // a NaN code in either row wins
+            else if (f) a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq);  // infinities
             store_output(p, m, n, a, alpha, sr, split);
         }
 }

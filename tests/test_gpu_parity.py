@@ -206,6 +206,30 @@ def test_every_tile_config(dev, orc, cfg, shape, profile):
         api.force_tile(prev)
 
 
+# ---- dense specials ---------------------------------------------------------------
+@pytest.mark.parametrize("profile,S", [("hopper", 1), ("hopper", 3), ("ada-pairwise", 5)])
+def test_dense_specials(dev, orc, profile, S):
+    """Many NaN rows (x) and E5M2 infinities with zeros (w), so that NaN rows,
+    Inf rows, Inf x 0 pairs and mixed-sign infinite products all occur, in
+    several splits: the NaN rows take the flag shortcut, the Inf rows the
+    per-output walk."""
+    gen = torch.Generator().manual_seed(77 + S)
+    rng = np.random.default_rng(77 + S)
+    M, N, K = 70, 96, 1040
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.05, 0.02, gen)
+    w = inject(random_codes((N, K), "e5m2", gen), "e5m2", 0.3, 0.02, gen)
+    for m in rng.choice(M, 30, replace=False):
+        x[m, rng.integers(0, K)] = int(rng.choice([0x7F, 0xFF]))
+    for n in rng.choice(N, 40, replace=False):
+        for _ in range(int(rng.integers(1, 3))):
+            w[n, rng.integers(0, K)] = int(rng.choice([0x7C, 0xFC]))
+    for n in rng.choice(N, 5, replace=False):
+        w[n, rng.integers(0, K)] = 0x7E  # e5m2 NaN
+    for out in ("bf16", "fp32", "e4m3fn"):
+        check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, out, True, S, f"dense specials {profile}",
+              profile=profile)
+
+
 # ---- FP8 outputs ------------------------------------------------------------------
 @pytest.mark.parametrize("seed", range(16))
 def test_fp8_outputs(dev, orc, seed):
