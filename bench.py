@@ -44,12 +44,13 @@ def log(msg):
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the library's kernel sources (csrc/, sorted by name)."""
+    """sha256 over the GEMM library's sources (csrc/emu_* and fp_round.h,
+    sorted by name)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_exact_fp8_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.startswith("emu_") or name == "fp_round.h":
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()

@@ -61,5 +61,17 @@ def build(output: str = OUTPUT, extra_flags=None, verbose: bool = False, jobs: i
     return output
 
 
+MICROBENCH_OUTPUT = os.path.join(PKG, "libemu_microbench.so")
+
+
+def build_microbench(output: str = MICROBENCH_OUTPUT, verbose: bool = False) -> str:
+    """The issue-rate microbenchmark (measurement only, not part of the GEMM)."""
+    tmp = output + ".tmp"
+    _run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "microbench.hip"), "-o", tmp], verbose)
+    os.replace(tmp, output)
+    return output
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_microbench(verbose=True))

@@ -370,17 +370,26 @@ __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve,
     }
 }
 
-// Row flags of four packed codes: bit 0 for any NaN or Inf code, bit 1 for
-// a NaN code (E4M3FN: magnitude 0x7F; E5M2: magnitude above 0x7C, Inf being
-// 0x7C).
+// Any NaN (E4M3FN) or Inf / NaN (E5M2) code among four packed codes: the
+// high bit of each byte of the result.
 template <int FMT>
-__device__ __forceinline__ uint32_t special_flags(uint32_t v)
+__device__ __forceinline__ uint32_t has_special(uint32_t v)
 {
-    const uint32_t mag = v & 0x7F7F7F7Fu;
-    if (FMT == FMT_E4M3) return (((mag + 0x01010101u) & 0x80808080u) != 0) ? 3u : 0u;
-    const uint32_t any = (mag + 0x04040404u) & 0x80808080u;  // magnitude >= 0x7C
-    const uint32_t nan = (mag + 0x03030303u) & 0x80808080u;  // magnitude >= 0x7D
-    return (any ? 1u : 0u) | (nan ? 2u : 0u);
+    if (FMT == FMT_E4M3) return ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    return ((v & 0x7C7C7C7Cu) + 0x04040404u) & 0x80808080u;
+}
+
+// Row flags of a 16-byte chunk that holds a special code: bit 0 always,
+// bit 1 if one of them is a NaN (E4M3FN: every special; E5M2: magnitude
+// above 0x7C, the infinity).
+template <int FMT>
+__device__ __forceinline__ uint32_t special_flags(uint4 raw)
+{
+    if (FMT == FMT_E4M3) return 3u;
+    const uint32_t nan = (((raw.x & 0x7F7F7F7Fu) + 0x03030303u) | ((raw.y & 0x7F7F7F7Fu) + 0x03030303u) |
+                          ((raw.z & 0x7F7F7F7Fu) + 0x03030303u) | ((raw.w & 0x7F7F7F7Fu) + 0x03030303u)) &
+                         0x80808080u;
+    return nan ? 3u : 1u;
 }
 
 template <int FMT>
@@ -635,8 +644,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 const int st = idx / NCHUNK, c = idx % NCHUNK;
                 const int r = c >> 1, half = c & 1;
                 if (r < BM) {
-                    myflag[q] |= special_flags<XF>(raw[q].x) | special_flags<XF>(raw[q].y) |
-                                 special_flags<XF>(raw[q].z) | special_flags<XF>(raw[q].w);
+                    if (has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) | has_special<XF>(raw[q].z) |
+                        has_special<XF>(raw[q].w))
+                        myflag[q] |= special_flags<XF>(raw[q]);  // rare: NaN / Inf codes
                     float *xa = xa_all + st * XA;
                     uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XP;
                     if (MX)
@@ -649,8 +659,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                                                   xe + r * P_STRIDE + 8 * half, xs + r * P_STRIDE + 8 * half);
                 } else {
                     const int rw = r - BM;
-                    myflag[q] |= special_flags<WF>(raw[q].x) | special_flags<WF>(raw[q].y) |
-                                 special_flags<WF>(raw[q].z) | special_flags<WF>(raw[q].w);
+                    if (has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) | has_special<WF>(raw[q].z) |
+                        has_special<WF>(raw[q].w))
+                        myflag[q] |= special_flags<WF>(raw[q]);  // rare: NaN / Inf codes
                     float *wa = wa_all + st * WA;
                     uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WP;
                     if (MX)
