@@ -31,6 +31,16 @@ struct MainParams {
     int64_t tps;
     int S;
     int fast;              // 1: one chain per split; 0: restart every 128 along the split
+    // Slow mode with chunk results stored (chunked = 1): grid z is
+    // S * chunk_groups; workgroup z takes split z / chunk_groups and the
+    // chunks_per_group 128-chunks of group z % chunk_groups of that split's
+    // k-list, and writes each chunk's chain result to out as partial
+    // (split * cps + chunk) (+0 for chunks past the k-list), to be added in
+    // order by the combine kernel.  Otherwise chunk_groups = 1, chunked = 0.
+    int chunked;
+    int chunk_groups;
+    int chunks_per_group;
+    int cps;               // chunks per split in the partial layout
     int out_kind;          // OutKind
     void *out;             // OUT_ACC_F32 / epilogue destination, [M, N] with row stride ldo elements
     int64_t ldo;
@@ -40,8 +50,9 @@ struct MainParams {
 };
 
 struct CombineParams {
-    const float *part;     // [S, M, N] partials, dense
+    const float *part;     // [S * cps, M, N] partials, dense
     int S, M, N;
+    int cps;               // partials per split: 1, or the slow-mode chunk results to add in order first
     int pairwise;          // 0: serial p0 + p1 + ...; 1: stride-halving pairwise tree
     int out_kind;          // OUT_ACC_F32 or an epilogue kind
     void *out;

@@ -23,10 +23,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     const int64_t total = (int64_t)p.M * p.N;
     if (idx >= total) return;
     const int64_t m = idx / p.N, n = idx - m * p.N;
+    // split s's partial: its single partial, or the running binary32 sum of
+    // its slow-mode chunk results in order from +0 (chunk results are never
+    // -0, so the first add reproduces the first chunk bit for bit)
+    auto split_partial = [&](int s) {
+        const float *q = p.part + (int64_t)s * p.cps * total + idx;
+        if (p.cps == 1) return q[0];
+        float a = 0.0f;
+        for (int c = 0; c < p.cps; ++c) a = a + q[(int64_t)c * total];
+        return a;
+    };
     float acc;
     if (!p.pairwise) {
-        acc = p.part[idx];
-        for (int s = 1; s < p.S; ++s) acc = acc + p.part[(int64_t)s * total + idx];
+        acc = split_partial(0);
+        for (int s = 1; s < p.S; ++s) acc = acc + split_partial(s);
     } else {
         int L = 0;
         while ((1 << L) < p.S) ++L;
@@ -36,7 +46,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
         for (int j = 0; j < (1 << L); ++j) {
             const int i = L ? (int)(__brev((unsigned)j) >> (32 - L)) : 0;
             bool hv = i < p.S;
-            float v = hv ? p.part[(int64_t)i * total + idx] : 0.0f;
+            float v = hv ? split_partial(i) : 0.0f;
             int l = 0;
             for (int jj = j; jj & 1; jj >>= 1, ++l) {
                 if (have[l] && hv) v = pend[l] + v;

@@ -443,16 +443,17 @@ __device__ __forceinline__ SplitSeq split_seq(const MainParams &p, int z)
     return q;
 }
 
-// The non-finite result of one output over a split's k-list: NaN if some k
-// pairs an infinity with a zero or infinite products of both signs occur,
-// otherwise the signed infinity.  Called only when a row holds an E5M2
-// infinity (rows with a NaN code resolve to the canonical NaN without it),
-// so the result is never finite; it also honours NaN codes, for clarity.
+// The non-finite result of one output over positions [p0, p1) of a split's
+// k-list: NaN if a NaN code is in either row, if some k pairs an infinity
+// with a zero, or if infinite products of both signs occur; otherwise the
+// signed infinity; 0 (not a result: the range is finite) when no product
+// there involves a NaN or Inf code.  Called only for rows flagged as holding
+// such codes.
 template <int XF, int WF>
-__device__ uint32_t special_acc(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq)
+__device__ uint32_t special_scan(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq, int64_t p0, int64_t p1)
 {
     bool nan = false, pos = false, neg = false;
-    for (int64_t i = 0; i < sq.len; ++i) {
+    for (int64_t i = p0; i < p1; ++i) {
         const int64_t k = sq.k_of(i);
         bool an, ai, az, bn, bi, bz;
         uint32_t as, bs;
@@ -466,7 +467,8 @@ __device__ uint32_t special_acc(const uint8_t *xr, const uint8_t *wr, const Spli
         }
     }
     if (nan || (pos && neg)) return kCanonNan32;
-    return neg ? 0xFF800000u : 0x7F800000u;
+    if (neg) return 0xFF800000u;
+    return pos ? 0x7F800000u : 0u;
 }
 
 __device__ __forceinline__ void store_output(const MainParams &p, int64_t m, int64_t n, uint32_t acc,
@@ -574,9 +576,14 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     int tile_m, tile_n;
     tile_order(tile_m, tile_n);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-    const int split = blockIdx.z;
+    const int split = blockIdx.z / p.chunk_groups, group = blockIdx.z % p.chunk_groups;
     const SplitSeq sq = split_seq(p, split);
     const int64_t tile_mask = (int64_t(1) << p.tile_shift) - 1;
+    // positions [pos_begin, pos_end) of the split's k-list: all of them, or
+    // one group of 128-chunks when chunk results are stored
+    const int64_t span = (int64_t)p.chunks_per_group * CHUNK;
+    const int64_t pos_begin = p.chunked ? (int64_t)group * span : 0;
+    const int64_t pos_end = p.chunked ? ((pos_begin + span < sq.len) ? pos_begin + span : sq.len) : sq.len;
 
     for (int i = t; i < BM + BN; i += NT) flags[i] = 0;
 
@@ -601,7 +608,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 const int st = idx / NCHUNK, c = idx % NCHUNK;
                 const int r = c >> 1, half = c & 1;
                 const int64_t sp = pos + (int64_t)st * KB;
-                if (sp < sq.len) {
+                if (sp < pos_end) {
                     const int64_t kb = sq.k_of(sp);
                     const int64_t tile_end = kb - (sp & tile_mask) + tile_mask + 1;
                     const int64_t lim = tile_end < p.K ? tile_end : p.K;
@@ -634,8 +641,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             for (int j = 0; j < (FAST ? 1 : RN); ++j) slow[i][j] = 0u;
     }
 
-    if (sq.len > 0) load_block(0);
-    for (int64_t pos = 0; pos < sq.len; pos += (int64_t)KB * SS) {
+    if (pos_begin < pos_end) load_block(pos_begin);
+    for (int64_t pos = pos_begin; pos < pos_end; pos += (int64_t)KB * SS) {
         __syncthreads();  // previous stages' readers are done with the LDS planes
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
@@ -677,12 +684,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         }
         __syncthreads();
         // prefetch the next stages; latency hidden by the compute below
-        if (pos + (int64_t)KB * SS < sq.len) load_block(pos + (int64_t)KB * SS);
+        if (pos + (int64_t)KB * SS < pos_end) load_block(pos + (int64_t)KB * SS);
 
 #pragma unroll 1
         for (int st = 0; st < SS; ++st) {
         const int64_t spos = pos + (int64_t)st * KB;
-        if (spos >= sq.len) break;  // uniform across the workgroup
+        if (spos >= pos_end) break;  // uniform across the workgroup
         const float *xa = xa_all + st * XA, *wa = wa_all + st * WA;
         const uint32_t *xe = xe_all + (MX ? 0 : st * XP), *we = we_all + (MX ? 0 : st * WP);
         const uint32_t *xs = xs_all + st * XP, *wsg = wsg_all + st * WP;
@@ -845,9 +852,22 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 }
         }
 
-        // slow accumulation: add the chunk result every 128 positions of the
-        // split's k-list, in order
-        if (!FAST && (((spos + KB) & (CHUNK - 1)) == 0 || spos + KB >= sq.len)) {
+        // slow accumulation: every 128 positions of the split's k-list the
+        // chunk result is added to the running sum, in order, or stored as a
+        // partial for the combine kernel to add
+        const bool chunk_end = ((spos + KB) & (CHUNK - 1)) == 0 || spos + KB >= pos_end;
+        if (!FAST && chunk_end && p.chunked) {
+            const int64_t part = (int64_t)split * p.cps + spos / CHUNK;
+            uint32_t *o = reinterpret_cast<uint32_t *>(p.out) + part * p.split_stride;
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) {
+                    const int64_t m = m0 + row_of(i), n = n0 + col_of(j);
+                    if (m < p.M && n < p.N && lane_g == 0) o[m * p.ldo + n] = c[i][j];
+                    c[i][j] = 0u;
+                }
+        } else if (!FAST && chunk_end) {
             uint32_t dep = 0;
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -876,6 +896,34 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     }
     __syncthreads();
 
+    if (p.chunked) {
+        // chunk partials: +0 for this group's chunks past the k-list; rows
+        // with NaN / Inf codes overwrite the chunks that hold them
+        const int c_lo = group * p.chunks_per_group;
+        const int c_hi = (c_lo + p.chunks_per_group < p.cps) ? c_lo + p.chunks_per_group : p.cps;
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) {
+                const int rm = row_of(i), rn = col_of(j);
+                const int64_t m = m0 + rm, n = n0 + rn;
+                if (m >= p.M || n >= p.N || lane_g != 0) continue;
+                const uint32_t f = flags[rm] | flags[BM + rn];
+                for (int ch = c_lo; ch < c_hi; ++ch) {
+                    uint32_t *o = reinterpret_cast<uint32_t *>(p.out) + ((int64_t)split * p.cps + ch) * p.split_stride;
+                    const int64_t cs = (int64_t)ch * CHUNK;
+                    if (cs >= sq.len) {
+                        o[m * p.ldo + n] = 0u;
+                    } else if (f) {
+                        const int64_t ce = (cs + CHUNK < sq.len) ? cs + CHUNK : sq.len;
+                        const uint32_t v = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, cs, ce);
+                        if (v) o[m * p.ldo + n] = v;
+                    }
+                }
+            }
+        return;
+    }
+
     uint32_t alpha = 0, sr = 0x3F800000u;  // the scales are read only when the epilogue runs here
     if (p.out_kind != OUT_ACC_F32) {
         alpha = mul_f32(__float_as_uint(*p.scale_x), __float_as_uint(*p.scale_w));
@@ -891,7 +939,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
             const uint32_t f = flags[rm] | flags[BM + rn];
             if (f & 2u) a = kCanonNan32;  // a NaN code in either row wins
-            else if (f) a = special_acc<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq);  // infinities
+            else if (f) a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len);  // infinities
             store_output(p, m, n, a, alpha, sr, split);
         }
 }

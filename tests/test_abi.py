@@ -239,3 +239,17 @@ def test_force_tile_range(lib):
         assert api.force_tile(-1) == len(api.TILE_CONFIGS) - 1
     finally:
         api.force_tile(prev)
+
+
+def test_workspace_for_chunked_slow_accumulation(lib):
+    """Slow accumulation on an output grid too small to fill the GPU stores
+    its 128-chunk results (S * chunks * M * N binary32 values) for the combine
+    kernel; fast accumulation and large grids need no such array."""
+    assert api.workspace_bytes(256, 4096, 4096, 1, False) == 32 * 256 * 4096 * 4
+    assert api.workspace_bytes(256, 4096, 4096, 1, True) == 0
+    assert api.workspace_bytes(8192, 8192, 8192, 1, False) == 0       # enough tiles already
+    assert api.workspace_bytes(16, 256, 65536, 8, False) == 8 * 64 * 16 * 256 * 4
+    assert api.workspace_bytes(16, 256, 65536, 8, True) == 8 * 16 * 256 * 4
+    assert api.workspace_bytes(64, 64, 128, 1, False) == 0            # a single chunk
+    # ada: 64-wide tiles dealt round-robin; the longest split sets the chunk count
+    assert api.workspace_bytes(16, 64, 640, 3, False, "ada-serial") == 3 * 2 * 16 * 64 * 4
