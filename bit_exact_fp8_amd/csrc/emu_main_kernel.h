@@ -530,7 +530,12 @@ struct WavesPerSimd {
 // wave per 16 rows: the wave's 16 x (16*RN) output tile is RN 16x16
 // matrix-instruction tiles, and lane l owns rows 4*(l/16) + i and columns
 // l%16 + 16*j, the layout of v_mfma_f32_16x16x16_bf16's result.
-template <int XF, int WF, int BM, int BN, int RM, int RN, int G, bool FAST, bool MX, int BLK, int SS>
+// Accumulation styles (template parameter ACC): one chain per split; slow
+// accumulation with the running binary32 sum in registers; slow
+// accumulation with each 128-chunk's result stored as a partial.
+constexpr int ACC_FAST = 0, ACC_SLOW = 1, ACC_SLOW_CHUNKS = 2;
+
+template <int XF, int WF, int BM, int BN, int RM, int RN, int G, int ACC, bool MX, int BLK, int SS>
 __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
@@ -548,6 +553,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr int K4PL = BLK / 4 / G;      // groups of 4 products per lane and block
     static_assert(WPL % WU == 0 && K4PL >= 1, "block slice per lane");
     static_assert(SS >= 1 && (!MX || SS == 1), "stages per barrier: matrix-core exponents use one");
+    constexpr bool FAST = ACC == ACC_FAST, CHUNKS = ACC == ACC_SLOW_CHUNKS;
     constexpr int XA = BM * A_STRIDE, XP = BM * P_STRIDE, WA = BN * A_STRIDE, WP = BN * P_STRIDE;
 
     // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
@@ -576,14 +582,15 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     int tile_m, tile_n;
     tile_order(tile_m, tile_n);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-    const int split = blockIdx.z / p.chunk_groups, group = blockIdx.z % p.chunk_groups;
+    const int split = CHUNKS ? blockIdx.z / p.chunk_groups : blockIdx.z;
+    const int group = CHUNKS ? blockIdx.z % p.chunk_groups : 0;
     const SplitSeq sq = split_seq(p, split);
     const int64_t tile_mask = (int64_t(1) << p.tile_shift) - 1;
     // positions [pos_begin, pos_end) of the split's k-list: all of them, or
     // one group of 128-chunks when chunk results are stored
     const int64_t span = (int64_t)p.chunks_per_group * CHUNK;
-    const int64_t pos_begin = p.chunked ? (int64_t)group * span : 0;
-    const int64_t pos_end = p.chunked ? ((pos_begin + span < sq.len) ? pos_begin + span : sq.len) : sq.len;
+    const int64_t pos_begin = CHUNKS ? (int64_t)group * span : 0;
+    const int64_t pos_end = CHUNKS ? ((pos_begin + span < sq.len) ? pos_begin + span : sq.len) : sq.len;
 
     for (int i = t; i < BM + BN; i += NT) flags[i] = 0;
 
@@ -629,16 +636,17 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     uint32_t tok = mode_round_toward_zero();
 
     uint32_t c[RM][RN];
-    uint32_t slow[FAST ? 1 : RM][FAST ? 1 : RN];
+    constexpr bool RUNNING = ACC == ACC_SLOW;  // a running slow sum per output
+    uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j) c[i][j] = 0u;
-    if (!FAST) {
+    if (RUNNING) {
 #pragma unroll
-        for (int i = 0; i < (FAST ? 1 : RM); ++i)
+        for (int i = 0; i < (RUNNING ? RM : 1); ++i)
 #pragma unroll
-            for (int j = 0; j < (FAST ? 1 : RN); ++j) slow[i][j] = 0u;
+            for (int j = 0; j < (RUNNING ? RN : 1); ++j) slow[i][j] = 0u;
     }
 
     if (pos_begin < pos_end) load_block(pos_begin);
@@ -856,7 +864,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         // chunk result is added to the running sum, in order, or stored as a
         // partial for the combine kernel to add
         const bool chunk_end = ((spos + KB) & (CHUNK - 1)) == 0 || spos + KB >= pos_end;
-        if (!FAST && chunk_end && p.chunked) {
+        if (CHUNKS && chunk_end) {
             const int64_t part = (int64_t)split * p.cps + spos / CHUNK;
             uint32_t *o = reinterpret_cast<uint32_t *>(p.out) + part * p.split_stride;
 #pragma unroll
@@ -867,7 +875,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     if (m < p.M && n < p.N && lane_g == 0) o[m * p.ldo + n] = c[i][j];
                     c[i][j] = 0u;
                 }
-        } else if (!FAST && chunk_end) {
+        } else if (RUNNING && chunk_end) {
             uint32_t dep = 0;
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -876,9 +884,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             const uint32_t tok_rn = mode_round_nearest_after(dep);
             uint32_t dep2 = 0;
 #pragma unroll
-            for (int i = 0; i < (FAST ? 1 : RM); ++i)
+            for (int i = 0; i < (RUNNING ? RM : 1); ++i)
 #pragma unroll
-                for (int j = 0; j < (FAST ? 1 : RN); ++j) {
+                for (int j = 0; j < (RUNNING ? RN : 1); ++j) {
                     slow[i][j] = add_rn(slow[i][j], c[i][j], tok_rn);
                     dep2 |= slow[i][j];
                     c[i][j] = 0u;
@@ -896,7 +904,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     }
     __syncthreads();
 
-    if (p.chunked) {
+    if constexpr (CHUNKS) {
         // chunk partials: +0 for this group's chunks past the k-list; rows
         // with NaN / Inf codes overwrite the chunks that hold them
         const int c_lo = group * p.chunks_per_group;
@@ -936,7 +944,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             const int rm = row_of(i), rn = col_of(j);
             const int64_t m = m0 + rm, n = n0 + rn;
             if (m >= p.M || n >= p.N || lane_g != 0) continue;
-            uint32_t a = FAST ? c[i][j] : slow[FAST ? 0 : i][FAST ? 0 : j];
+            uint32_t a = FAST ? c[i][j] : slow[RUNNING ? i : 0][RUNNING ? j : 0];
             const uint32_t f = flags[rm] | flags[BM + rn];
             if (f & 2u) a = kCanonNan32;  // a NaN code in either row wins
             else if (f) a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len);  // infinities
@@ -950,9 +958,13 @@ hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
     constexpr int NT = (BM / RM) * (BN / RN) * G;
     dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, S);
     if (p.fast)
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, true, MX, BLK, SS>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, ACC_FAST, MX, BLK, SS>), grid, dim3(NT), 0, stream,
+                           p);
+    else if (p.chunked)
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, ACC_SLOW_CHUNKS, MX, BLK, SS>), grid, dim3(NT), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, false, MX, BLK, SS>), grid, dim3(NT), 0, stream,
+        hipLaunchKernelGGL((main_kernel<XF, WF, BM, BN, RM, RN, G, ACC_SLOW, MX, BLK, SS>), grid, dim3(NT), 0, stream,
                            p);
     return hipGetLastError();
 }
