@@ -207,12 +207,14 @@ def test_every_tile_config(dev, orc, cfg, shape, profile):
 
 
 # ---- dense specials ---------------------------------------------------------------
-@pytest.mark.parametrize("profile,S", [("hopper", 1), ("hopper", 3), ("ada-pairwise", 5)])
-def test_dense_specials(dev, orc, profile, S):
+@pytest.mark.parametrize("profile,S,fast", [("hopper", 1, True), ("hopper", 3, True), ("ada-pairwise", 5, True),
+                                            ("hopper", 1, False), ("ada-serial", 2, False)])
+def test_dense_specials(dev, orc, profile, S, fast):
     """Many NaN rows (x) and E5M2 infinities with zeros (w), so that NaN rows,
     Inf rows, Inf x 0 pairs and mixed-sign infinite products all occur, in
     several splits: the NaN rows take the flag shortcut, the Inf rows the
-    per-output walk."""
+    per-output walk; in slow mode on this small grid the chunk results are
+    stored and the chunks holding special codes rescanned."""
     gen = torch.Generator().manual_seed(77 + S)
     rng = np.random.default_rng(77 + S)
     M, N, K = 70, 96, 1040
@@ -225,8 +227,9 @@ def test_dense_specials(dev, orc, profile, S):
             w[n, rng.integers(0, K)] = int(rng.choice([0x7C, 0xFC]))
     for n in rng.choice(N, 5, replace=False):
         w[n, rng.integers(0, K)] = 0x7E  # e5m2 NaN
+    assert fast or api.workspace_bytes(M, N, K, S, fast, profile) > (S > 1) * S * M * N * 4  # chunked
     for out in ("bf16", "fp32", "e4m3fn"):
-        check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, out, True, S, f"dense specials {profile}",
+        check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, out, fast, S, f"dense specials {profile}",
               profile=profile)
 
 
