@@ -807,8 +807,10 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     }
             }
 
-            // pass 2: truncated terms, signs, accumulation
-#pragma unroll 1
+            // pass 2: truncated terms, signs, accumulation (small thread tiles
+            // unroll twice, so the next LDS reads overlap this iteration's
+            // arithmetic: they run at 1-2 waves per SIMD)
+#pragma unroll(RM * RN <= 4 ? 2 : 1)
             for (int k4 = hb * (BLK / 4) + lane_g * K4PL; k4 < hb * (BLK / 4) + (lane_g + 1) * K4PL; ++k4) {
                 float4 av[RM], bv[RN];
                 uint2 sa[RM], sb[RN];
