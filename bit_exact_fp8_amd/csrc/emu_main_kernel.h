@@ -741,7 +741,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 for (int i = 0; i < RM; ++i)
 #pragma unroll
                     for (int j = 0; j < RN; ++j) gmax[i][j] = 0u;
-#pragma unroll 1
+#pragma unroll(RM * RN <= 4 ? 2 : 1)
                 for (int wo = hb * WPB + lane_g * WPL; wo < hb * WPB + (lane_g + 1) * WPL; wo += WU) {
                     if constexpr (WU == 4) {
                         uint4 ea[RM], eb[RN];
