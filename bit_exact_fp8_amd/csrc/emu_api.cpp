@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/emu_fp8gemm.h"
+#include "emu_chain.h"
 #include "emu_internal.h"
 #include "fp_round.h"
 
@@ -349,5 +350,10 @@ uint16_t emu_host_f32_to_bf16(uint32_t f) { return emu::f32_to_bf16(f); }
 uint16_t emu_host_f32_to_f16(uint32_t f) { return emu::f32_to_f16(f); }
 uint8_t emu_host_f32_to_e4m3fn(uint32_t f) { return emu::f32_to_fp8_sat<true>(f); }
 uint8_t emu_host_f32_to_e5m2(uint32_t f) { return emu::f32_to_fp8_sat<false>(f); }
+uint32_t emu_host_block_step(uint32_t c, const uint8_t *x, int x_fmt, const uint8_t *w, int w_fmt, int n)
+{
+    if (n < 0 || n > 32 || !x || !w) return 0xFFFFFFFFu;
+    return emu::block_step_codes(c, x, x_fmt == EMU_FP8_E5M2, w, w_fmt == EMU_FP8_E5M2, n);
+}
 
 }  // extern "C"
