@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--tile", type=int, default=-1, help="force a tile configuration (tuning)")
     ap.add_argument("--profile", default="hopper", choices=sorted(api.PROFILE),
                     help="arithmetic profile (hopper is the pages' default)")
+    ap.add_argument("--inf-density", type=float, default=0.0, metavar="P",
+                    help="replace a fraction P of the e5m2 operand's codes by +-Inf (specials throughput)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -157,6 +159,16 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {wl.name} inputs (seed {args.seed})")
     x, w = make_operands(wl, args.seed)
+    if args.inf_density > 0:
+        if "e5m2" not in (wl.xfmt, wl.wfmt):
+            print("bench.py: --inf-density needs an e5m2 operand", file=sys.stderr)
+            sys.exit(2)
+        t = w if wl.wfmt == "e5m2" else x
+        gen = torch.Generator().manual_seed(args.seed + 2000)
+        hit = torch.rand(t.shape, generator=gen) < args.inf_density
+        signs = torch.randint(0, 2, t.shape, generator=gen, dtype=torch.uint8) << 7
+        t[hit] = signs[hit] | 0x7C
+        log(f"[bench] {int(hit.sum())} infinities in {'w' if t is w else 'x'}")
     xd = x.to(dev).view(FP8_DTYPES[wl.xfmt])
     wd = w.to(dev).view(FP8_DTYPES[wl.wfmt])
     sxd = torch.tensor([wl.scale_x], dtype=torch.float32, device=dev)
@@ -200,7 +212,7 @@ def main():
     value = ops * args.steps / wall
     achieved = ops / (launch_ms * 1e-3)
 
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name) if args.inf_density == 0 and args.profile == "hopper" else None
     result = {
         "metric": METRIC,
         "value": value,
@@ -214,7 +226,8 @@ def main():
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {**wl.describe(), "profile": args.profile, "parallelism": "single GPU"},
+        "config": {**wl.describe(), "profile": args.profile, "parallelism": "single GPU",
+                   **({"inf_density": args.inf_density} if args.inf_density > 0 else {})},
         "roofline": {
             "bound": "alu",
             "achieved": achieved / 1e12,

@@ -392,21 +392,6 @@ __device__ __forceinline__ uint32_t special_flags(uint4 raw)
     return nan ? 3u : 1u;
 }
 
-template <int FMT>
-__device__ __forceinline__ void classify(uint32_t code, bool &nan, bool &inf, bool &zero, uint32_t &sign)
-{
-    sign = code >> 7;
-    if (FMT == FMT_E4M3) {
-        nan = (code & 0x7Fu) == 0x7Fu;
-        inf = false;
-        zero = (code & 0x7Fu) == 0;
-    } else {
-        nan = (code & 0x7Cu) == 0x7Cu && (code & 3u);
-        inf = (code & 0x7Fu) == 0x7Cu;
-        zero = (code & 0x7Fu) == 0;
-    }
-}
-
 // The k-list of one split: positions 0 .. len-1 along its k-tiles (width
 // 2^shift; tile `first`, then every `stride`-th), k = tile * W + offset.
 struct SplitSeq {
@@ -443,30 +428,65 @@ __device__ __forceinline__ SplitSeq split_seq(const MainParams &p, int z)
     return q;
 }
 
+// Byte masks (the high bit of each byte) of four packed codes: zero, NaN
+// and infinite codes.
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t v)
+{
+    return ~((v & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t nan_bytes(uint32_t v)
+{
+    return ((v & 0x7F7F7F7Fu) + (FMT == FMT_E4M3 ? 0x01010101u : 0x03030303u)) & 0x80808080u;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t inf_bytes(uint32_t v)
+{
+    if (FMT == FMT_E4M3) return 0u;
+    return zero_bytes((v & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu);
+}
 // The non-finite result of one output over positions [p0, p1) of a split's
 // k-list: NaN if a NaN code is in either row, if some k pairs an infinity
 // with a zero, or if infinite products of both signs occur; otherwise the
 // signed infinity; 0 (not a result: the range is finite) when no product
-// there involves a NaN or Inf code.  Called only for rows flagged as holding
-// such codes.
+// there involves a NaN or Inf code.  Called only for outputs with a flagged
+// row (xflag, wflag: the row holds such codes in this workgroup's range).
+// The flagged rows are read 16 codes at a time; the other row only where a
+// flagged chunk holds a NaN / Inf code, so the work per output is one pass
+// over the flagged row(s), whatever the number of special codes.
 template <int XF, int WF>
-__device__ uint32_t special_scan(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq, int64_t p0, int64_t p1)
+__device__ uint32_t special_scan(const uint8_t *xr, const uint8_t *wr, const SplitSeq &sq, int64_t p0, int64_t p1,
+                             bool xflag, bool wflag)
 {
-    bool nan = false, pos = false, neg = false;
-    for (int64_t i = p0; i < p1; ++i) {
-        const int64_t k = sq.k_of(i);
-        bool an, ai, az, bn, bi, bz;
-        uint32_t as, bs;
-        classify<XF>(xr[k], an, ai, az, as);
-        classify<WF>(wr[k], bn, bi, bz, bs);
-        if (an || bn) nan = true;
-        else if (ai || bi) {
-            if (az || bz) nan = true;
-            else if (as ^ bs) neg = true;
-            else pos = true;
+    uint32_t bad = 0, pos = 0, neg = 0;
+    for (int64_t q = p0; q < p1; q += 16) {
+        const int64_t k = sq.k_of(q);
+        uint4 xv = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
+        uint32_t hit = 0;
+        if (xflag) {
+            xv = *reinterpret_cast<const uint4 *>(xr + k);
+            hit |= has_special<XF>(xv.x) | has_special<XF>(xv.y) | has_special<XF>(xv.z) | has_special<XF>(xv.w);
+        }
+        if (wflag) {
+            wv = *reinterpret_cast<const uint4 *>(wr + k);
+            hit |= has_special<WF>(wv.x) | has_special<WF>(wv.y) | has_special<WF>(wv.z) | has_special<WF>(wv.w);
+        }
+        if (!hit) continue;
+        if (!xflag) xv = *reinterpret_cast<const uint4 *>(xr + k);
+        if (!wflag) wv = *reinterpret_cast<const uint4 *>(wr + k);
+        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t a = xs[u], b = ws[u];
+            const uint32_t ai = inf_bytes<XF>(a), bi = inf_bytes<WF>(b);
+            const uint32_t inf = ai | bi;
+            const uint32_t neg_sign = (a ^ b) & 0x80808080u;
+            bad |= nan_bytes<XF>(a) | nan_bytes<WF>(b) | (ai & zero_bytes(b)) | (bi & zero_bytes(a));
+            neg |= inf & neg_sign;
+            pos |= inf & ~neg_sign;
         }
     }
-    if (nan || (pos && neg)) return kCanonNan32;
+    if (bad || (pos && neg)) return kCanonNan32;
     if (neg) return 0xFF800000u;
     return pos ? 0x7F800000u : 0u;
 }
@@ -565,7 +585,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     __shared__ __attribute__((aligned(16))) uint32_t wsg_all[SS * WP];
     __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
     __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
-    __shared__ uint32_t flags[BM + BN];
+    __shared__ uint32_t flags[BM + BN + CHUNKS];  // per row (and, for stored chunks, their union)
 
     const int t = threadIdx.x;
     const int lane_g = t % G, slot = t / G;
@@ -592,7 +612,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     const int64_t pos_begin = CHUNKS ? (int64_t)group * span : 0;
     const int64_t pos_end = CHUNKS ? ((pos_begin + span < sq.len) ? pos_begin + span : sq.len) : sq.len;
 
-    for (int i = t; i < BM + BN; i += NT) flags[i] = 0;
+    for (int i = t; i < BM + BN + CHUNKS; i += NT) flags[i] = 0;
 
     // chunk q of this thread: row r = idx >> 1 (x rows first), half = idx & 1
     uint32_t myflag[CPT];
@@ -902,7 +922,10 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
         const int idx = t + q * NT;
-        if (idx < NCHUNK * SS && myflag[q]) atomicOr(&flags[(idx % NCHUNK) >> 1], myflag[q]);
+        if (idx < NCHUNK * SS && myflag[q]) {
+            atomicOr(&flags[(idx % NCHUNK) >> 1], myflag[q]);
+            if (CHUNKS) atomicOr(&flags[BM + BN], myflag[q]);
+        }
     }
     __syncthreads();
 
@@ -911,6 +934,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         // with NaN / Inf codes overwrite the chunks that hold them
         const int c_lo = group * p.chunks_per_group;
         const int c_hi = (c_lo + p.chunks_per_group < p.cps) ? c_lo + p.chunks_per_group : p.cps;
+        if ((int64_t)(c_hi - 1) * CHUNK < sq.len && !flags[BM + BN]) return;  // uniform: nothing to overwrite
 #pragma unroll
         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -926,7 +950,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         o[m * p.ldo + n] = 0u;
                     } else if (f) {
                         const int64_t ce = (cs + CHUNK < sq.len) ? cs + CHUNK : sq.len;
-                        const uint32_t v = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, cs, ce);
+                        const uint32_t v = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, cs, ce,
+                                                                flags[rm] != 0, flags[BM + rn] != 0);
                         if (v) o[m * p.ldo + n] = v;
                     }
                 }
@@ -949,7 +974,9 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             uint32_t a = FAST ? c[i][j] : slow[RUNNING ? i : 0][RUNNING ? j : 0];
             const uint32_t f = flags[rm] | flags[BM + rn];
             if (f & 2u) a = kCanonNan32;  // a NaN code in either row wins
-            else if (f) a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len);  // infinities
+            else if (f)  // infinities
+                a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len, flags[rm] != 0,
+                                         flags[BM + rn] != 0);
             store_output(p, m, n, a, alpha, sr, split);
         }
 }

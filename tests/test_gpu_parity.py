@@ -233,6 +233,57 @@ def test_dense_specials(dev, orc, profile, S, fast):
               profile=profile)
 
 
+def _inf_rows_and_columns(e5_rows: int, other_rows: int, K: int, seed: int):
+    """Codes with whole rows of infinities, rows with exactly SPL = 8 and 9
+    16-code chunks holding infinities (the per-row chunk list's capacity and
+    its overflow), single infinities next to zeros, NaN codes, and partner
+    rows that are zero-free and of one sign (so that +Inf and -Inf results
+    occur as well as NaN)."""
+    gen = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    e5 = inject(random_codes((e5_rows, K), "e5m2", gen), "e5m2", 0.05, 0.02, gen)
+    ot = inject(random_codes((other_rows, K), "e4m3fn", gen), "e4m3fn", 0.05, 0.02, gen)
+    e5[1, :] = 0x7C                                                  # +Inf row
+    e5[2, :] = torch.from_numpy(rng.choice([0x7C, 0xFC], K).astype(np.uint8))  # Inf row, both signs
+    for r, nchunks, codes in ((3, 8, [0x7C]), (4, 9, [0xFC]), (5, 8, [0x7C, 0xFC]), (6, 1, [0x7C])):
+        for c in rng.choice(K // 16, nchunks, replace=False):
+            e5[r, 16 * c + rng.integers(0, 16)] = int(rng.choice(codes))
+    e5[7, rng.integers(0, K)] = 0x7D                                 # e5m2 NaN
+    e5[8, 0], e5[8, K - 1] = 0xFC, 0xFC                              # first and last k
+    pos = ot[0, :] & 0x7F
+    pos[pos == 0] = 0x01
+    pos[pos == 0x7F] = 0x7E
+    ot[0, :] = pos                                                   # zero-free, positive
+    ot[1, :] = ot[0, :] | 0x80                                       # zero-free, negative
+    ot[2, :] = ot[0, :]
+    ot[2, 16 * 5 + 3] = 0x00                                         # one zero
+    ot[3, rng.integers(0, K)] = 0xFF                                 # e4m3fn NaN
+    return e5, ot
+
+
+@pytest.mark.parametrize("cfg", [-1, 1, 5, 6])
+@pytest.mark.parametrize("profile,S,fast", [("hopper", 1, True), ("hopper", 3, True), ("ada-pairwise", 5, True),
+                                            ("hopper", 1, False), ("ada-serial", 2, False)])
+def test_inf_rows_and_columns(dev, orc, profile, S, fast, cfg):
+    """Rows and columns of infinities (validation page, claims table: NaN
+    and Inf rows and columns through the GEMM epilogue), on both operands,
+    with the automatic tile and forced ones (one lane per output, four
+    lanes per output, matrix-core exponents)."""
+    K = 1040
+    prev = api.force_tile(cfg)
+    try:
+        for e5_is_x in (True, False):
+            e5, ot = _inf_rows_and_columns(40 if e5_is_x else 48, 48 if e5_is_x else 40, K, 5 + S)
+            if e5_is_x:
+                x, xfmt, w, wfmt = e5, "e5m2", ot, "e4m3fn"
+            else:
+                x, xfmt, w, wfmt = ot, "e4m3fn", e5, "e5m2"
+            check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", fast, S,
+                  f"inf rows {xfmt}x{wfmt} {profile} tile {cfg}", profile=profile)
+    finally:
+        api.force_tile(prev)
+
+
 # ---- FP8 outputs ------------------------------------------------------------------
 @pytest.mark.parametrize("seed", range(16))
 def test_fp8_outputs(dev, orc, seed):
