@@ -1,8 +1,9 @@
 """Build libemu_fp8gemm.so for gfx950 with hipcc (in-tree, next to this file).
 
 The main kernel's variants (block width x format pair) are separate
-translation units of emu_variant.hip, compiled in parallel and linked with
-the dispatcher, the combine kernel and the C ABI."""
+translation units of emu_variant.hip (and of emu_spec_variant.hip for the
+exponent-speculation kernels), compiled in parallel and linked with the
+dispatcher, the combine kernel and the C ABI."""
 from __future__ import annotations
 
 import os
@@ -34,8 +35,10 @@ def _units(objdir: str):
     units = [(os.path.join(CSRC, "emu_kernels.hip"), os.path.join(objdir, "emu_kernels.o"), []),
              (os.path.join(CSRC, "emu_api.cpp"), os.path.join(objdir, "emu_api.o"), [])]
     for b, xf, wf in VARIANTS:
-        units.append((os.path.join(CSRC, "emu_variant.hip"), os.path.join(objdir, f"emu_variant_{b}_{xf}{wf}.o"),
-                      [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]))
+        defs = [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]
+        units.append((os.path.join(CSRC, "emu_variant.hip"), os.path.join(objdir, f"emu_variant_{b}_{xf}{wf}.o"), defs))
+        units.append((os.path.join(CSRC, "emu_spec_variant.hip"), os.path.join(objdir, f"emu_spec_{b}_{xf}{wf}.o"),
+                      defs))
     return units
 
 

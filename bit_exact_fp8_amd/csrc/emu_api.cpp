@@ -54,12 +54,47 @@ struct Plan {
     int chunk_groups;
     int chunks_per_group;
     int cps;
+    // fast accumulation with speculated block exponents (see make_plan)
+    int spec;
+    int spec_cfg;
+    int64_t nbs;
+    int guess_perturb;
+    // workspace layout: [split partials][range-start guesses][block words]
+    int64_t part_bytes, guess_bytes, pk_bytes;
 };
 
 constexpr int64_t kChunk = 128;                          // slow-accumulation restart
 constexpr int64_t kChunkWaveTarget = 4096;               // 4 waves on each SIMD
 constexpr int64_t kMaxChunkWorkspace = int64_t(1) << 30; // bytes of stored chunk results
 constexpr int64_t kResidentWgs = 256 * 3;                // 64x64 workgroups resident at once
+constexpr int64_t kMaxSpecWorkspace = int64_t(1) << 31;  // bytes of block words
+
+// Exponent speculation forced through emu_debug_force_spec (-1: automatic).
+std::atomic<int> g_forced_spec{-1};
+// Tile configuration forced through emu_debug_force_tile (-1: automatic).
+std::atomic<int> g_forced_tile{-1};
+
+// The number of 128-chunks per group, from cps down to 1, whose workgroup
+// count (tiles per group times groups) best fills whole rounds of `resident`
+// workgroups, at least two rounds (one round leaves CUs idle while the last
+// workgroups finish).
+int64_t fill_groups(int64_t cps, int64_t tiles, int S, int64_t resident)
+{
+    int64_t best_cpg = cps;
+    double best_fill = -1.0;
+    for (int64_t cpg = cps; cpg >= 1; --cpg) {
+        const int64_t groups = (cps + cpg - 1) / cpg;
+        if (groups * S > kMaxSplits) break;
+        const int64_t wgs = tiles * groups;
+        const int64_t rounds = (wgs + resident - 1) / resident;
+        const double fill = (double)wgs / (double)(rounds * resident) * (rounds >= 2 ? 1.0 : 0.5);
+        if (fill > best_fill + 1e-9) {
+            best_fill = fill;
+            best_cpg = cpg;
+        }
+    }
+    return best_cpg;
+}
 
 Plan make_plan(emu_profile profile, int64_t M, int64_t N, int64_t K, int S, int fast)
 {
@@ -96,19 +131,7 @@ Plan make_plan(emu_profile profile, int64_t M, int64_t N, int64_t K, int S, int 
         const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64) * (int64_t)S;
         const int64_t bytes = (int64_t)S * cps * M * N * 4;
         if (cps >= 2 && tiles64 * 4 < kChunkWaveTarget && bytes <= kMaxChunkWorkspace) {
-            int64_t best_cpg = cps;
-            double best_fill = -1.0;
-            for (int64_t cpg = cps; cpg >= 1; --cpg) {
-                const int64_t groups = (cps + cpg - 1) / cpg;
-                if (groups * S > kMaxSplits) break;
-                const int64_t wgs = tiles64 * groups;
-                const int64_t rounds = (wgs + kResidentWgs - 1) / kResidentWgs;
-                const double fill = (double)wgs / (double)(rounds * kResidentWgs) * (rounds >= 2 ? 1.0 : 0.5);
-                if (fill > best_fill + 1e-9) {
-                    best_fill = fill;
-                    best_cpg = cpg;
-                }
-            }
+            const int64_t best_cpg = fill_groups(cps, tiles64, S, kResidentWgs);
             const int64_t groups = (cps + best_cpg - 1) / best_cpg;
             if (groups >= 2) {
                 p.chunked = 1;
@@ -118,11 +141,59 @@ Plan make_plan(emu_profile profile, int64_t M, int64_t N, int64_t K, int S, int 
             }
         }
     }
+    // Fast accumulation is one sequential chain per output and split; with
+    // few outputs the chains alone cannot fill the GPU.  The block step
+    // needs the incoming accumulator only through its exponent (where it
+    // joins the alignment) and its truncated value (which adds to the
+    // block's sum), so the blocks can be formed in parallel along K from
+    // guessed exponents, and a short walk per chain then applies each
+    // block's stored sum, or recomputes the block exactly where the guess
+    // chose a different alignment exponent than the true accumulator: the
+    // result is the chain's, bit for bit.  On MI355X this path measured
+    // slower than the direct one on the workloads it was built for (the
+    // 64 x 5760 x 1920 projection: guess, block words and walk together
+    // 0.36 ms against 0.18 ms; the 16 x 256 x 65536 split-K one: 0.95 ms
+    // against 0.13 ms): the walk's lanes wait for each other's rare
+    // recomputed blocks, and the short K ranges pay their pipeline start.
+    // It is therefore only planned when forced (emu_debug_force_spec), for
+    // fast accumulation whose block words fit in 2 GiB.
+    p.spec = 0;
+    p.spec_cfg = emu::TILE_64x64_MX;
+    p.nbs = 0;
+    p.guess_perturb = 0;
+    p.part_bytes = (p.chunked ? (int64_t)S * p.cps : (S > 1 ? (int64_t)S : 0)) * M * N * 4;
+    p.guess_bytes = p.pk_bytes = 0;
+    const int forced_spec = g_forced_spec.load(std::memory_order_relaxed);
+    const int forced_tile = g_forced_tile.load(std::memory_order_relaxed);
+    if (fast && nt > 0 && M > 0 && N > 0 && forced_spec > 0) {
+        const int64_t tiles_max = p.round_robin ? (nt + S - 1) / S : p.tps;
+        const int64_t max_len = (tiles_max * W < K) ? tiles_max * W : K;
+        const int64_t cps = (max_len + kChunk - 1) / kChunk;
+        const int64_t nbs = (max_len + p.block - 1) / p.block;
+        const int cfg = (forced_tile == emu::TILE_64x64_MX || forced_tile == emu::TILE_16x64_MX) ? forced_tile
+                        : (forced_tile >= 0)                                                  ? -1
+                        : (M <= 16)                                                           ? emu::TILE_16x64_MX
+                                                                                              : emu::TILE_64x64_MX;
+        const int64_t pk_bytes = (int64_t)S * nbs * M * N * 4;
+        if (cfg >= 0 && pk_bytes <= kMaxSpecWorkspace && M <= kMaxGridY * 16) {
+            const emu::TileShape t = emu::tile_shape(cfg);
+            const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * (int64_t)S;
+            // workgroups resident per CU: 16x64 (one wave, 29 KB of LDS) 5, 64x64 2
+            const int64_t resident = 256 * (cfg == emu::TILE_16x64_MX ? 5 : 2);
+            const int64_t cpg = fill_groups(cps, tiles, S, resident);
+            p.spec = 1;
+            p.spec_cfg = cfg;
+            p.nbs = nbs;
+            p.cps = (int)cps;
+            p.chunks_per_group = (int)cpg;
+            p.chunk_groups = (int)((cps + cpg - 1) / cpg);
+            p.guess_perturb = forced_spec >= 2 ? forced_spec - 1 : 0;
+            p.guess_bytes = (int64_t)S * p.chunk_groups * M * N * 4;
+            p.pk_bytes = pk_bytes;
+        }
+    }
     return p;
 }
-
-// Tile configuration forced through emu_debug_force_tile (-1: automatic).
-std::atomic<int> g_forced_tile{-1};
 
 // Pick the tile configuration with the best expected throughput: its
 // measured steady-state efficiency on MI355X (fraction of the integer-VALU
@@ -179,6 +250,86 @@ emu_status check_common(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const 
     return EMU_OK;
 }
 
+// The combine kernel over S split partials (or chunk results) in `part`.
+emu_status launch_combine_of(const Plan &plan, const float *part, int S, int64_t M, int64_t N, int out_kind,
+                             void *out, int64_t ldo, const float *sx, const float *sw, const float *sr,
+                             hipStream_t stream)
+{
+    emu::CombineParams c{};
+    c.part = part;
+    c.S = S;
+    c.cps = plan.spec ? 1 : plan.cps;
+    c.pairwise = plan.pairwise;
+    c.M = (int)M;
+    c.N = (int)N;
+    c.out_kind = out_kind;
+    c.out = out;
+    c.ldo = ldo;
+    c.scale_x = sx;
+    c.scale_w = sw;
+    c.scale_result = sr;
+    hipError_t e = emu::launch_combine(c, stream);
+    if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    return EMU_OK;
+}
+
+// Fast accumulation with speculated exponents: guess, block words, walk
+// (and the combine kernel for S > 1).
+emu_status run_spec(const Plan &plan, const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w,
+                    emu_fp8_format wf, int64_t ldw, int64_t M, int64_t N, int64_t K, const float *sx,
+                    const float *sw, const float *sr, void *out, int out_kind, int64_t ldo, int S, void *workspace,
+                    hipStream_t stream)
+{
+    char *ws = static_cast<char *>(workspace);
+    emu::MainParams p{};
+    p.x = x;
+    p.w = w;
+    p.ldx = ldx;
+    p.ldw = ldw;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = K;
+    p.tile_shift = plan.tile_shift;
+    p.round_robin = plan.round_robin;
+    p.tps = plan.tps;
+    p.S = S;
+    p.fast = 1;
+    p.chunk_groups = plan.chunk_groups;
+    p.chunks_per_group = plan.chunks_per_group;
+    p.cps = plan.cps;
+    p.scale_x = sx;
+    p.scale_w = sw;
+    p.scale_result = sr;
+    p.spec = 1;
+    p.guess = reinterpret_cast<float *>(ws + plan.part_bytes);
+    p.pk = reinterpret_cast<uint32_t *>(ws + plan.part_bytes + plan.guess_bytes);
+    p.nbs = plan.nbs;
+    p.guess_perturb = plan.guess_perturb;
+    if (S > 1) {
+        p.out_kind = emu::OUT_ACC_F32;
+        p.out = ws;
+        p.ldo = N;
+        p.split_stride = M * N;
+    } else {
+        p.out_kind = out_kind;
+        p.out = out;
+        p.ldo = ldo;
+        p.split_stride = 0;
+    }
+    const char *names[3] = {"guess", "block-word", "walk"};
+    for (int which = 0; which < 3; ++which) {
+        hipError_t e = emu::launch_spec(which, plan.spec_cfg, plan.block, xf, wf, p, S * plan.chunk_groups, stream);
+        if (e != hipSuccess)
+            return fail(EMU_ERR_DEVICE, std::string(names[which]) + " kernel launch: " + hipGetErrorString(e));
+    }
+    if (S > 1) {
+        emu_status st = launch_combine_of(plan, reinterpret_cast<const float *>(ws), S, M, N, out_kind, out, ldo, sx,
+                                          sw, sr, stream);
+        if (st != EMU_OK) return st;
+    }
+    return ok();
+}
+
 emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *w, emu_fp8_format wf,
                int64_t ldw, int64_t M, int64_t N, int64_t K, const float *sx, const float *sw,
                const float *sr, void *out,
@@ -187,6 +338,9 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
 {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     const Plan plan = make_plan(profile, M, N, K, S, fast);
+    if (plan.spec)
+        return run_spec(plan, x, xf, ldx, w, wf, ldw, M, N, K, sx, sw, sr, out, out_kind, ldo, S, workspace,
+                        stream);
     const int Z = S * plan.chunk_groups;  // grid z: splits, times chunk groups
     const int cfg = choose_tile(M, N, Z);
     const emu::TileShape ts = emu::tile_shape(cfg);
@@ -232,21 +386,9 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
         if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("main kernel launch: ") + hipGetErrorString(e));
     }
     if (partials) {
-        emu::CombineParams c{};
-        c.part = static_cast<const float *>(workspace);
-        c.S = S;
-        c.cps = plan.cps;
-        c.pairwise = plan.pairwise;
-        c.M = (int)M;
-        c.N = (int)N;
-        c.out_kind = out_kind;
-        c.out = out;
-        c.ldo = ldo;
-        c.scale_x = sx;
-        c.scale_w = sw;
-        c.scale_result = sr;
-        hipError_t e = emu::launch_combine(c, stream);
-        if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("combine kernel launch: ") + hipGetErrorString(e));
+        emu_status st = launch_combine_of(plan, static_cast<const float *>(workspace), S, M, N, out_kind, out, ldo,
+                                          sx, sw, sr, stream);
+        if (st != EMU_OK) return st;
     }
     (void)workspace_bytes;
     return ok();
@@ -260,9 +402,7 @@ size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fas
 {
     if (M < 0 || N < 0 || K < 0 || split_S < 1 || split_S > kMaxSplits) return 0;
     const Plan plan = make_plan(profile, M, N, K, split_S, fast_accum);
-    if (plan.chunked) return (size_t)split_S * (size_t)plan.cps * (size_t)M * (size_t)N * sizeof(float);
-    if (split_S == 1) return 0;
-    return (size_t)split_S * (size_t)M * (size_t)N * sizeof(float);
+    return (size_t)(plan.part_bytes + plan.guess_bytes + plan.pk_bytes);
 }
 
 emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
@@ -342,6 +482,12 @@ int emu_debug_force_tile(int cfg)
 {
     if (cfg < -1 || cfg >= emu::TILE_COUNT) return -2;
     return g_forced_tile.exchange(cfg);
+}
+
+int emu_debug_force_spec(int mode)
+{
+    if (mode < -1 || mode > 3) return -2;
+    return g_forced_spec.exchange(mode);
 }
 
 uint32_t emu_host_mul_f32(uint32_t a, uint32_t b) { return emu::mul_f32(a, b); }

@@ -47,6 +47,16 @@ struct MainParams {
     int64_t split_stride;  // elements between consecutive splits' partials in `out` (S > 1)
     const float *scale_x, *scale_w;
     const float *scale_result;  // FP8 outputs only; null means 1
+    // Exponent speculation (fast accumulation, spec = 1): grid z is
+    // S * chunk_groups as for stored chunks; workgroup z forms the block
+    // words of its range into pk[(split * nbs + block) * M * N + m * N + n],
+    // starting from the guesses guess[z * M * N + m * N + n] that the guess
+    // kernel writes; the walk kernel then runs each chain over the words.
+    int spec;
+    float *guess;
+    uint32_t *pk;
+    int64_t nbs;           // blocks per split in the pk layout
+    int guess_perturb;     // testing: 0 none, 1 range-start guesses 0, 2 four times too large
 };
 
 struct CombineParams {
@@ -64,7 +74,7 @@ struct CombineParams {
 // Tile configurations of the main kernel: rows x cols per workgroup; per
 // thread 4x8, 4x4, 2x4, 2x2 outputs, or one output chain shared by 2 or 4
 // lanes (G2, G4; these stage 8 K-blocks per barrier); MX: block exponent
-// maxima on the matrix cores.
+// maxima on the matrix cores (16x64: one wave, for few rows).
 enum TileConfig : int {
     TILE_64x128 = 0,
     TILE_64x64 = 1,
@@ -75,7 +85,8 @@ enum TileConfig : int {
     TILE_64x64_MX = 6,
     TILE_64x128_MX = 7,
     TILE_16x8_G4 = 8,
-    TILE_COUNT = 9
+    TILE_16x64_MX = 9,
+    TILE_COUNT = 10
 };
 
 struct TileShape {
@@ -92,6 +103,12 @@ hipError_t launch_main(int cfg, int block, int xfmt, int wfmt, const MainParams 
 // emu_variant.hip.
 template <int BLK, int XF, int WF>
 hipError_t launch_variant(int cfg, const MainParams &p, int S, hipStream_t stream);
+template <int BLK, int XF, int WF>
+hipError_t launch_variant_spec(int which, int cfg, const MainParams &p, int Z, hipStream_t stream);
+// The speculation's guess (which = 0), block-word main kernel (1, tile
+// configuration cfg, grid z = Z) or walk (2) kernel.
+hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const MainParams &p, int Z,
+                       hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 
 }  // namespace emu

@@ -80,6 +80,7 @@ TileShape tile_shape(int cfg)
     case TILE_64x64_MX: return {64, 64, 256};
     case TILE_64x128_MX: return {64, 128, 256};
     case TILE_16x8_G4: return {16, 8, 512};
+    case TILE_16x64_MX: return {16, 64, 64};
     default: return {64, 128, 256};
     }
 }
@@ -94,6 +95,20 @@ hipError_t launch_main(int cfg, int block, int xfmt, int wfmt, const MainParams 
     case (16 << 4) | 0: return launch_variant<16, 0, 0>(cfg, p, S, stream);
     case (16 << 4) | 1: return launch_variant<16, 0, 1>(cfg, p, S, stream);
     case (16 << 4) | 2: return launch_variant<16, 1, 0>(cfg, p, S, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const MainParams &p, int Z, hipStream_t stream)
+{
+    const int key = (block << 4) | (xfmt << 1) | wfmt;
+    switch (key) {
+    case (32 << 4) | 0: return launch_variant_spec<32, 0, 0>(which, cfg, p, Z, stream);
+    case (32 << 4) | 1: return launch_variant_spec<32, 0, 1>(which, cfg, p, Z, stream);
+    case (32 << 4) | 2: return launch_variant_spec<32, 1, 0>(which, cfg, p, Z, stream);
+    case (16 << 4) | 0: return launch_variant_spec<16, 0, 0>(which, cfg, p, Z, stream);
+    case (16 << 4) | 1: return launch_variant_spec<16, 0, 1>(which, cfg, p, Z, stream);
+    case (16 << 4) | 2: return launch_variant_spec<16, 1, 0>(which, cfg, p, Z, stream);
     default: return hipErrorInvalidValue;
     }
 }

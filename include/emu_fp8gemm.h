@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define EMU_ABI_VERSION 2
+#define EMU_ABI_VERSION 3
 
 #if defined(EMU_BUILDING_LIBRARY)
 #define EMU_API __attribute__((visibility("default")))
@@ -153,8 +153,13 @@ EMU_API emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_
                           int fast_accum, int split_S, emu_profile profile,
                           void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device workspace the two calls above need: split_S * M * N * 4 bytes when
- * split_S > 1, otherwise 0.  Returns 0 for invalid sizes. */
+/* Device workspace in bytes that the two calls above need for these
+ * arguments (0 for invalid sizes): split partials (split_S * M * N * 4 when
+ * split_S > 1), the results of groups of 128-K chunks when slow accumulation
+ * over a small output grid stores them, or, for fast accumulation over a
+ * small output grid with long chains, the exponent-speculation arrays (one
+ * 4-byte word per 32 or 16 products of every output, plus one guess per
+ * output and K range).  Depends on the plan only, never on the data. */
 EMU_API size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum,
                            emu_profile profile);
 
@@ -172,15 +177,27 @@ EMU_API int emu_abi_version(void);
 /*
  * Testing and tuning: force the main kernel's tile configuration for every
  * later call in the process (cfg = -1 restores the automatic choice; valid
- * configurations are 0 .. 8: 64x128, 64x64, 32x64, 32x32 output tiles with
+ * configurations are 0 .. 9: 64x128, 64x64, 32x64, 32x32 output tiles with
  * one lane per output, 16x16 with 2 or 4 lanes per output, 64x64 and
  * 64x128 with the block exponent maxima on the matrix cores, 16x8 with 4
- * lanes per output).  Results do not
+ * lanes per output, 16x64 with matrix-core maxima in one wave).  Results do not
  * depend on the configuration.  Returns the previous setting, or -2 (and
  * changes nothing) for an invalid cfg.  Process-wide; not for concurrent use
  * with calls that expect the automatic choice.
  */
 EMU_API int emu_debug_force_tile(int cfg);
+
+/*
+ * Testing and tuning: force the exponent-speculation plan for fast
+ * accumulation (mode -1: automatic; 0: never; 1: whenever the forced or
+ * automatic tile allows it; 2, 3: as 1, with the guesses at the start of
+ * every K range replaced by 0 (2) or by four times their value (3), so that
+ * many blocks take the exact recomputation).  Results do not depend on the
+ * mode.  The mode also changes emu_workspace_bytes.  Returns the previous
+ * mode, or -2 (and changes nothing) for an invalid mode.  Process-wide, like
+ * emu_debug_force_tile.
+ */
+EMU_API int emu_debug_force_spec(int mode);
 
 /*
  * Host builds of the library's own IEEE rounding routines, the same source

@@ -47,7 +47,7 @@ def test_abi_version(lib):
     """The library reports the EMU_ABI_VERSION of the header it was built with."""
     hdr = open(os.path.join(ROOT, "include", "emu_fp8gemm.h")).read()
     want = int(hdr.split("#define EMU_ABI_VERSION")[1].split()[0])
-    assert api.abi_version() == want == 2
+    assert api.abi_version() == want == 3
 
 
 def test_status_strings(lib):
@@ -58,7 +58,45 @@ def test_status_strings(lib):
 def test_workspace_bytes():
     assert api.workspace_bytes(16, 256, 65536, 8) == 8 * 16 * 256 * 4
     assert api.workspace_bytes(64, 5760, 1920, 1) == 0
+    assert api.workspace_bytes(8192, 8192, 8192, 1) == 0
     assert api._lib().emu_workspace_bytes(-1, 16, 16, 2, 1, 0) == 0
+
+
+@pytest.mark.parametrize("M,N,K,S,profile,block", [(16, 256, 65536, 8, "hopper", 32), (64, 5760, 1920, 1, "hopper", 32),
+                                                   (16, 256, 65536, 8, "ada-pairwise", 16)])
+def test_workspace_for_speculation(M, N, K, S, profile, block):
+    """With the speculated block exponents forced, the workspace holds the
+    split partials (S > 1), one guess per output, split and K range (1 to
+    ceil(K / S / 128) ranges) and one word per block of every chain."""
+    prev = api.force_spec("on")
+    try:
+        ws = api.workspace_bytes(M, N, K, S, True, profile)
+    finally:
+        api.force_spec(prev)
+    part = S * M * N * 4 if S > 1 else 0
+    tile = 128 if profile == "hopper" else 64
+    nt = -(-K // tile)
+    tiles_max = -(-nt // S)
+    max_len = min(tiles_max * tile, K)
+    nbs = -(-max_len // block)
+    pk = S * nbs * M * N * 4
+    rest = ws - part - pk
+    assert rest > 0 and rest % (S * M * N * 4) == 0
+    assert 1 <= rest // (S * M * N * 4) <= -(-max_len // 128)
+
+
+def test_force_spec(lib):
+    """The speculation modes are accepted and returned; others are refused
+    without changing the setting."""
+    prev = api.force_spec("auto")
+    try:
+        for mode in api.SPEC_MODES:
+            api.force_spec(mode)
+        assert api.force_spec("auto") == "on-guess-x4"
+        assert lib.emu_debug_force_spec(4) == -2 and lib.emu_debug_force_spec(-2) == -2
+        assert api.force_spec("auto") == "auto"
+    finally:
+        api.force_spec(prev)
 
 
 def call(lib, x=16, xf=0, ldx=32, w=16, wf=0, ldw=32, M=4, N=16, K=32, sx=4, sw=4, sr=None, out=16,
@@ -244,12 +282,11 @@ def test_force_tile_range(lib):
 def test_workspace_for_chunked_slow_accumulation(lib):
     """Slow accumulation on an output grid too small to fill the GPU stores
     its 128-chunk results (S * chunks * M * N binary32 values) for the combine
-    kernel; fast accumulation and large grids need no such array."""
+    kernel; large grids need no such array."""
     assert api.workspace_bytes(256, 4096, 4096, 1, False) == 32 * 256 * 4096 * 4
     assert api.workspace_bytes(256, 4096, 4096, 1, True) == 0
     assert api.workspace_bytes(8192, 8192, 8192, 1, False) == 0       # enough tiles already
     assert api.workspace_bytes(16, 256, 65536, 8, False) == 8 * 64 * 16 * 256 * 4
-    assert api.workspace_bytes(16, 256, 65536, 8, True) == 8 * 16 * 256 * 4
     assert api.workspace_bytes(64, 64, 128, 1, False) == 0            # a single chunk
     # ada: 64-wide tiles dealt round-robin; the longest split sets the chunk count
     assert api.workspace_bytes(16, 64, 640, 3, False, "ada-serial") == 3 * 2 * 16 * 64 * 4

@@ -284,6 +284,72 @@ def test_inf_rows_and_columns(dev, orc, profile, S, fast, cfg):
         api.force_tile(prev)
 
 
+# ---- exponent speculation -------------------------------------------------------------
+SPEC_SHAPES = [(1, 16, 48, 1), (37, 80, 1040, 1), (17, 48, 4096, 3), (70, 144, 2064, 5), (16, 256, 8192, 8),
+               (5, 32, 640, 12)]
+
+
+@pytest.mark.parametrize("tile", [-1, 6, 9])
+@pytest.mark.parametrize("profile", ["hopper", "ada-pairwise", "ada-serial"])
+@pytest.mark.parametrize("mode", ["on", "on-guess-zero", "on-guess-x4"])
+def test_speculation(dev, orc, mode, profile, tile):
+    """Fast accumulation through the speculated block exponents (guess, block
+    words, walk), forced on ragged shapes, several splits (some of them
+    empty), both tiles that form block words, three format pairs and every
+    output kind; with the guesses as computed, and with the guesses of every
+    K range replaced by 0 or by four times their value, so that most blocks
+    are recomputed from their codes by the walk."""
+    prev_spec = api.force_spec(mode)
+    prev_tile = api.force_tile(tile)
+    try:
+        for idx, (M, N, K, S) in enumerate(SPEC_SHAPES):
+            xfmt, wfmt = [("e4m3fn", "e5m2"), ("e5m2", "e4m3fn"), ("e4m3fn", "e4m3fn")][idx % 3]
+            out = ["bf16", "fp32", "fp16", "e4m3fn", "bf16", "fp32"][idx]
+            wl = Workload("s", M, N, K, xfmt=xfmt, wfmt=wfmt, x_sigma=40.0, w_sigma=8.0 if wfmt == "e4m3fn" else 300.0,
+                          zero_frac=0.05, subnormal_frac=0.02)
+            x, w = make_operands(wl, 7 + idx)
+            check(dev, orc, x, xfmt, w, wfmt, 1 / 64, 1 / 32, out, True, S,
+                  f"speculation {mode} tile {tile} #{idx}", profile=profile)
+    finally:
+        api.force_tile(prev_tile)
+        api.force_spec(prev_spec)
+
+
+@pytest.mark.parametrize("mode", ["on", "on-guess-zero"])
+@pytest.mark.parametrize("profile,S", [("hopper", 1), ("hopper", 3), ("ada-pairwise", 5)])
+def test_speculation_specials(dev, orc, mode, profile, S):
+    """NaN and Inf rows and columns through the speculated path: the block
+    words of a range with special codes are marked and the walk applies the
+    specials rule to the whole chain."""
+    prev = api.force_spec(mode)
+    try:
+        K = 1040
+        for e5_is_x in (True, False):
+            e5, ot = _inf_rows_and_columns(40 if e5_is_x else 48, 48 if e5_is_x else 40, K, 11 + S)
+            if e5_is_x:
+                x, xfmt, w, wfmt = e5, "e5m2", ot, "e4m3fn"
+            else:
+                x, xfmt, w, wfmt = ot, "e4m3fn", e5, "e5m2"
+            check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", True, S,
+                  f"speculation specials {mode} {xfmt}x{wfmt}", profile=profile)
+    finally:
+        api.force_spec(prev)
+
+
+@pytest.mark.parametrize("name", ["proj_64x5760x1920", "splitk_16x256x65536_s8"])
+def test_speculation_workload(dev, orc, name):
+    """The projection and split-K workloads at full size through the
+    speculated path (forced), against the oracle on every output."""
+    wl = WORKLOADS[name]
+    x, w = make_operands(wl, 5)
+    prev = api.force_spec("on")
+    try:
+        check(dev, orc, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S,
+              f"speculation {name}")
+    finally:
+        api.force_spec(prev)
+
+
 # ---- FP8 outputs ------------------------------------------------------------------
 @pytest.mark.parametrize("seed", range(16))
 def test_fp8_outputs(dev, orc, seed):
