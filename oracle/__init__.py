@@ -106,6 +106,9 @@ class Oracle:
             ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, _U32P, _U32P, ctypes.c_int]
+        L.oracle_accumulate_c.argtypes = [
+            _U8P, ctypes.c_int, ctypes.c_int64, _U8P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, _U32P, ctypes.c_int, ctypes.c_int, _U32P]
 
     @property
     def mutant(self) -> int:
@@ -194,6 +197,25 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return acc, y
+
+
+    def accumulate_c(self, x, xfmt, w, wfmt, c_in, profile=None):
+        """The fast-accumulation chain of every output started from the
+        incoming binary32 accumulators c_in (uint32 bit patterns [M, N])
+        instead of +0; one split.  Returns the accumulators (uint32 [M, N])."""
+        pf = resolve_profile(profile)
+        x = np.ascontiguousarray(x, dtype=np.uint8)
+        w = np.ascontiguousarray(w, dtype=np.uint8)
+        M, K = x.shape
+        N = w.shape[0]
+        c_in = np.ascontiguousarray(c_in, dtype=np.uint32)
+        assert c_in.shape == (M, N)
+        acc = np.zeros((M, N), dtype=np.uint32)
+        rc = self.lib.oracle_accumulate_c(_u8(x), FMT[xfmt], max(K, 1), _u8(w), FMT[wfmt], max(K, 1),
+                                          M, N, K, _u32(c_in), pf["B"], pf["F"], _u32(acc))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return acc
 
 
 def _u8(a):

@@ -62,6 +62,7 @@
 #define MUT_RR_TILE_DOUBLED   20  /* round-robin k-tiles twice as wide as the profile's */
 #define MUT_SR_FOLDED         21  /* scale_result folded into alpha instead of a separate multiply */
 #define MUT_FP8_NO_SATURATION 22  /* FP8 outputs overflow to NaN / Inf instead of saturating */
+#define MUT_C_OWN_EXPONENT    23  /* a binary32 subnormal c aligned at floor(log2|c|), not emin */
 
 /* ------------------------------------------------------------------------ */
 /* Public constants (mirrored in oracle/__init__.py).                        */
@@ -206,8 +207,12 @@ static int64_t scale_floor(int64_t m, int sh)
  * row on 32-product blocks and 13 fraction bits):
  *
  *  1. E is the largest alignment exponent among the nonzero products, and,
- *     when the incoming accumulator c is nonzero, floor(log2|c|) ("c enters in
- *     the block's alignment").  With nothing nonzero the block gives +0.
+ *     when the incoming accumulator c is nonzero, its exponent ("c enters in
+ *     the block's alignment"): floor(log2|c|), or binary32's emin -126 for a
+ *     subnormal c.  Reading: the pages fix emin for subnormal FP8 inputs
+ *     only; a binary32 c is taken the same way (an incoming c below 2^-126
+ *     only arises from a caller's accumulator input).  With nothing nonzero
+ *     the block gives +0.
  *  2. The quantum is 2^q with q = E - F: every term keeps F fraction bits
  *     relative to 2^E.
  *  3. Each term, and c, is cut to that quantum toward zero in sign-magnitude
@@ -229,6 +234,9 @@ static exact_val block_step(exact_val c, const product *p, int n, int F)
 #if ORACLE_MUTANT != MUT_C_NOT_IN_MAX
     if (c.mag != 0) {
         int ec = c.q + floor_log2_u64((uint64_t)c.mag);
+#if ORACLE_MUTANT != MUT_C_OWN_EXPONENT
+        if (ec < -126) ec = -126;
+#endif
         if (!have || ec > E) E = ec;
         have = 1;
     }
@@ -805,6 +813,56 @@ API int oracle_block_step(const int *g, const int *P, const int *s, int n, int F
     exact_val c = {c_neg, c_mag, c_q};
     exact_val r = block_step(c, buf, n, F);
     *neg = r.neg; *mag = r.mag; *q = r.q;
+    return 0;
+}
+
+/*
+ * The fast chain of one output started from an incoming binary32
+ * accumulator c_in instead of +0 (the accumulator-only path: validation page,
+ * claims table, a c passing through blocks without products, over all 2^32
+ * binary32 patterns).  Readings, the pages printing no rule: with K = 0 there
+ * is no block and c_in is returned unchanged (a NaN as the canonical NaN); a
+ * NaN c_in gives NaN; an infinite c_in stays that infinity unless the
+ * products hold a NaN code, an infinity times zero or the opposite infinity,
+ * which give NaN; a finite c_in with infinite products gives the products'
+ * result; -0 enters as +0.
+ */
+static uint32_t acc_bits_with_c(const operands *o, int64_t m, int64_t n, uint32_t c_in, const oracle_profile *pf)
+{
+    const uint32_t ce = (c_in >> 23) & 0xFFu, cm = c_in & 0x7FFFFFu;
+    if (ce == 0xFFu && cm) return CANON_NAN_F32;
+    if (o->K == 0) return c_in;
+    int neg = 0;
+    int cls = special_class(o, m, n, &neg);
+    if (ce == 0xFFu) {
+        if (cls == CLS_NAN) return CANON_NAN_F32;
+        if (cls == CLS_INF && neg != (int)(c_in >> 31)) return CANON_NAN_F32;
+        return c_in;
+    }
+    if (cls == CLS_NAN) return CANON_NAN_F32;
+    if (cls == CLS_INF) return neg ? 0xFF800000u : 0x7F800000u;
+    exact_val c = EXACT_PLUS_ZERO;
+    if (ce || cm) {
+        c.neg = (int)(c_in >> 31);
+        c.mag = ce ? (int64_t)(cm | 0x800000u) : (int64_t)cm;
+        c.q = ce ? (int)ce - 150 : -149;
+    }
+    kseq ks = kseq_range(0, o->K);
+    return f32_bits(exact_to_f32(chain_exact(o, m, n, &ks, 0, ks.len, pf, c)));
+}
+
+/* Fast accumulation, one split, from incoming accumulators c_in [M, N]
+ * (binary32 bit patterns, row stride N) into acc_out [M, N]. */
+API int oracle_accumulate_c(const uint8_t *x, int xfmt, int64_t ldx, const uint8_t *w, int wfmt, int64_t ldw,
+                            int64_t M, int64_t N, int64_t K, const uint32_t *c_in, int B, int F,
+                            uint32_t *acc_out)
+{
+    if (B < 1 || B > MAX_B || F < 1 || F > 23) return -1;
+    if ((xfmt != FMT_E4M3FN && xfmt != FMT_E5M2) || (wfmt != FMT_E4M3FN && wfmt != FMT_E5M2)) return -1;
+    operands o = {x, xfmt, ldx, w, wfmt, ldw, M, N, K};
+    oracle_profile pf = {B, F, 128, 128, LAYOUT_CONTIGUOUS, COMBINE_SERIAL};
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) acc_out[m * N + n] = acc_bits_with_c(&o, m, n, c_in[m * N + n], &pf);
     return 0;
 }
 

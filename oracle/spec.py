@@ -76,13 +76,15 @@ def block(c: Fraction, prods, F):
     """One block step.  prods: list of (value, alignment exponent) for the
     nonzero products; c the incoming accumulator (0 means +0).
 
-    E = max(alignment exponents, floor(log2|c|) if c != 0); every term and c
+    E = max(alignment exponents, c's exponent if c != 0); every term and c
     are cut toward zero to multiples of 2^(E-F); their exact sum is cut toward
     zero to F+1 significant bits; a zero sum is +0.  F=None keeps everything
-    exact."""
+    exact.  c's exponent is floor(log2|c|), or -126 (binary32's emin) for a
+    subnormal c: the reading that takes a binary32 c as the pages take
+    subnormal FP8 inputs (only a caller's incoming accumulator is that small)."""
     exps = [g for _, g in prods]
     if c != 0:
-        exps.append(floor_log2(abs(c)))
+        exps.append(max(floor_log2(abs(c)), -126))
     if not exps:
         return Fraction(0)
     if F is None:
@@ -97,11 +99,11 @@ def block(c: Fraction, prods, F):
     return trunc_to_quantum(total, Fraction(2) ** (lead - F))
 
 
-def chain(xrow, xfmt, wrow, wfmt, k0, k1, B, F, ks=None):
+def chain(xrow, xfmt, wrow, wfmt, k0, k1, B, F, ks=None, c0=Fraction(0)):
     """Blocks of B consecutive products (of range(k0, k1), or of the ordered
-    index list ks), each stepping the accumulator."""
+    index list ks), each stepping the accumulator, which starts at c0."""
     ks = list(range(k0, k1)) if ks is None else list(ks)
-    c = Fraction(0)
+    c = c0
     for i in range(0, len(ks), B):
         prods = []
         for k in ks[i:i + B]:
@@ -360,6 +362,27 @@ def accumulator(xrow, xfmt, wrow, wfmt, K, fast=True, S=1, B=32, F=13, Q=128, W=
         assert fast and S == 1, "unbounded bits only for one fast chain"
         return parts[0]
     return combine(parts, scheme)
+
+
+def accumulator_c_bits(xrow, xfmt, wrow, wfmt, K, c_bits, B=32, F=13) -> int:
+    """The fast chain of one output from the incoming binary32 accumulator
+    c_bits (one split), as bits.  Readings as in emu_oracle.c: K = 0 returns
+    c unchanged (NaN canonical); NaN c gives NaN; an infinite c stays, unless
+    the products give NaN or the opposite infinity (then NaN); -0 enters as
+    +0."""
+    c = f32_value(c_bits)
+    if isinstance(c, float) and math.isnan(c):
+        return CANON_NAN_32
+    if K == 0:
+        return c_bits
+    sp = special(xrow, xfmt, wrow, wfmt, K)
+    if isinstance(c, float):  # an infinity
+        if sp == "nan" or (sp is not None and (sp == "-inf") != (c < 0)):
+            return CANON_NAN_32
+        return c_bits
+    if sp is not None:
+        return {"nan": CANON_NAN_32, "+inf": 0x7F800000, "-inf": 0xFF800000}[sp]
+    return f32_bits_of(chain(xrow, xfmt, wrow, wfmt, 0, K, B, F, c0=c))
 
 
 def accumulator_bits(*args, **kw) -> int:

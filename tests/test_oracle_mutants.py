@@ -33,6 +33,7 @@ MUTANTS = {
     20: "round-robin k-tiles twice as wide",
     21: "scale_result folded into alpha",
     22: "FP8 outputs overflow instead of saturating",
+    23: "subnormal incoming accumulator aligned at its own exponent",
 }
 
 

@@ -57,3 +57,11 @@ def test_epilogue_random(o):
 
 def test_spec_cross_check(o):
     pins.pin_spec_cross_check(o)
+
+
+def test_accumulator_only_path(o):
+    pins.pin_c_only(o)
+
+
+def test_incoming_accumulator_composes_chains(o):
+    pins.pin_c_composition(o)
