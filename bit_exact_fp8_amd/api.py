@@ -57,6 +57,8 @@ def _lib():
     lib.emu_scaled_mm.restype = i32
     lib.emu_accumulate.argtypes = common + [vp, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.emu_accumulate.restype = i32
+    lib.emu_accumulate_c.argtypes = common + [vp, i64, vp, i64, i32, vp]
+    lib.emu_accumulate_c.restype = i32
     lib.emu_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
     lib.emu_workspace_bytes.restype = ctypes.c_size_t
     lib.emu_status_string.argtypes = [i32]
@@ -179,14 +181,26 @@ def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, sca
 
 
 def accumulate(x: torch.Tensor, w: torch.Tensor, use_fast_accum: bool, split_S: int = 1,
-               profile: str = "hopper") -> torch.Tensor:
+               profile: str = "hopper", c: torch.Tensor | None = None) -> torch.Tensor:
     """The fp32 accumulator before the epilogue.  Both operands are [rows, K]
     (user guide, section 3: accumulate takes w, not w.t(), and has no default
-    for use_fast_accum)."""
+    for use_fast_accum).  c: optional incoming accumulators ([M, N] float32,
+    row-major): the fast chains start from them instead of +0 (fast
+    accumulation and split_S = 1 only)."""
     xx, ww, M, N, K, ldx, ldw = _operands(x, w.t())
     dev = xx.device
     acc = torch.empty((M, N), dtype=torch.float32, device=dev)
     ldacc = acc.stride(0) if M > 1 else N
+    if c is not None:
+        if not use_fast_accum or split_S != 1:
+            raise EmuError(EMU_ERR_UNSUPPORTED, "incoming accumulators need fast accumulation and split_S = 1")
+        if c.shape != (M, N) or c.dtype != torch.float32 or c.device != dev or (N > 1 and c.stride(1) != 1):
+            raise ValueError("c must be a row-major [M, N] float32 tensor on the operands' device")
+        ldc = c.stride(0) if M > 1 else N
+        _check(_lib().emu_accumulate_c(xx.data_ptr(), _fmt(xx), ldx, ww.data_ptr(), _fmt(ww), ldw, M, N, K,
+                                       c.data_ptr(), ldc, acc.data_ptr(), ldacc, PROFILE[profile],
+                                       _stream_handle(dev)))
+        return acc
     ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
     wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     lib = _lib()

@@ -2,8 +2,9 @@
 
 The main kernel's variants (block width x format pair) are separate
 translation units of emu_variant.hip (and of emu_spec_variant.hip for the
-exponent-speculation kernels), compiled in parallel and linked with the
-dispatcher, the combine kernel and the C ABI."""
+exponent-speculation kernels, emu_cin_variant.hip for the chains from
+incoming accumulators), compiled in parallel and linked with the dispatcher,
+the combine kernel and the C ABI."""
 from __future__ import annotations
 
 import os
@@ -38,6 +39,8 @@ def _units(objdir: str):
         defs = [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]
         units.append((os.path.join(CSRC, "emu_variant.hip"), os.path.join(objdir, f"emu_variant_{b}_{xf}{wf}.o"), defs))
         units.append((os.path.join(CSRC, "emu_spec_variant.hip"), os.path.join(objdir, f"emu_spec_{b}_{xf}{wf}.o"),
+                      defs))
+        units.append((os.path.join(CSRC, "emu_cin_variant.hip"), os.path.join(objdir, f"emu_cin_{b}_{xf}{wf}.o"),
                       defs))
     return units
 

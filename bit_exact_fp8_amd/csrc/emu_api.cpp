@@ -461,6 +461,51 @@ emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, c
                ldacc, fast_accum, split_S, profile, workspace, workspace_bytes, stream);
 }
 
+emu_status emu_accumulate_c(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
+                            emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K, const float *c_in,
+                            int64_t ldc, float *acc, int64_t ldacc, emu_profile profile, void *stream)
+{
+    emu_status s = check_common(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, 1, profile);
+    if (s != EMU_OK) return s;
+    if (ldacc < N || ldc < N) return fail(EMU_ERR_INVALID_ARG, "ldacc or ldc smaller than N");
+    if (M == 0 || N == 0) return ok();
+    if (!acc || !c_in) return fail(EMU_ERR_INVALID_ARG, "null accumulator pointer");
+    if ((reinterpret_cast<uintptr_t>(acc) & 3u) || (reinterpret_cast<uintptr_t>(c_in) & 3u))
+        return fail(EMU_ERR_INVALID_ARG, "acc and c_in must be 4-byte aligned");
+    const Plan plan = make_plan(profile, M, N, K, 1, 1);
+    const int cfg = choose_tile(M, N, 1);
+    const emu::TileShape ts = emu::tile_shape(cfg);
+    const int64_t rows_per_launch = kMaxGridY * ts.bm;
+    emu::MainParams p{};
+    p.ldx = ldx;
+    p.ldw = ldw;
+    p.N = (int)N;
+    p.K = K;
+    p.tile_shift = plan.tile_shift;
+    p.round_robin = plan.round_robin;
+    p.tps = plan.tps;
+    p.S = 1;
+    p.fast = 1;
+    p.chunk_groups = 1;
+    p.chunks_per_group = 1;
+    p.cps = 1;
+    p.out_kind = emu::OUT_ACC_F32;
+    p.ldo = ldacc;
+    p.w = w;
+    p.ldc = ldc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    for (int64_t m_start = 0; m_start < M; m_start += rows_per_launch) {
+        const int64_t rows = (M - m_start < rows_per_launch) ? M - m_start : rows_per_launch;
+        p.x = x ? x + m_start * ldx : nullptr;
+        p.M = (int)rows;
+        p.c_in = c_in + m_start * ldc;
+        p.out = acc + m_start * ldacc;
+        hipError_t e = emu::launch_main_cin(cfg, plan.block, x_fmt, w_fmt, p, st);
+        if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("main kernel launch: ") + hipGetErrorString(e));
+    }
+    return ok();
+}
+
 const char *emu_status_string(emu_status status)
 {
     switch (status) {

@@ -57,6 +57,10 @@ struct MainParams {
     uint32_t *pk;
     int64_t nbs;           // blocks per split in the pk layout
     int guess_perturb;     // testing: 0 none, 1 range-start guesses 0, 2 four times too large
+    // Incoming accumulators (fast accumulation, S = 1): chain (m, n) starts
+    // from c_in[m * ldc + n] instead of +0.
+    const float *c_in;
+    int64_t ldc;
 };
 
 struct CombineParams {
@@ -109,6 +113,10 @@ hipError_t launch_variant_spec(int which, int cfg, const MainParams &p, int Z, h
 // configuration cfg, grid z = Z) or walk (2) kernel.
 hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const MainParams &p, int Z,
                        hipStream_t stream);
+template <int BLK, int XF, int WF>
+hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream);
+// The main kernel from incoming accumulators (grid z = 1).
+hipError_t launch_main_cin(int cfg, int block, int xfmt, int wfmt, const MainParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 
 }  // namespace emu

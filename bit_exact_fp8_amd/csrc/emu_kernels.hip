@@ -113,6 +113,20 @@ hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const 
     }
 }
 
+hipError_t launch_main_cin(int cfg, int block, int xfmt, int wfmt, const MainParams &p, hipStream_t stream)
+{
+    const int key = (block << 4) | (xfmt << 1) | wfmt;
+    switch (key) {
+    case (32 << 4) | 0: return launch_variant_cin<32, 0, 0>(cfg, p, stream);
+    case (32 << 4) | 1: return launch_variant_cin<32, 0, 1>(cfg, p, stream);
+    case (32 << 4) | 2: return launch_variant_cin<32, 1, 0>(cfg, p, stream);
+    case (16 << 4) | 0: return launch_variant_cin<16, 0, 0>(cfg, p, stream);
+    case (16 << 4) | 1: return launch_variant_cin<16, 0, 1>(cfg, p, stream);
+    case (16 << 4) | 2: return launch_variant_cin<16, 1, 0>(cfg, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream)
 {
     const int64_t total = (int64_t)p.M * p.N;

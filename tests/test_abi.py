@@ -154,6 +154,20 @@ def test_accumulate_rejections(lib):
     assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 16, 16, 1, 3, 0, 16, 3 * 4 * 16 * 4 - 1, None) == api.EMU_ERR_WORKSPACE
 
 
+def test_accumulate_c_rejections(lib):
+    """emu_accumulate_c checks its arguments on the host (fake device
+    addresses, never dereferenced)."""
+    f = lib.emu_accumulate_c
+    #     x   xf ldx  w  wf ldw  M  N   K   c_in ldc acc ldacc prof stream
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 16, 8, 16, 16, 0, None) == api.EMU_ERR_INVALID_ARG   # ldc < N
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 0, 16, 16, 16, 0, None) == api.EMU_ERR_INVALID_ARG   # null c_in
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 18, 16, 16, 16, 0, None) == api.EMU_ERR_INVALID_ARG  # misaligned
+    assert f(16, 1, 32, 16, 1, 32, 4, 16, 32, 16, 16, 16, 16, 0, None) == api.EMU_ERR_REJECTED     # e5m2 x e5m2
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 24, 16, 16, 16, 16, 0, None) == api.EMU_ERR_REJECTED     # K % 16
+    assert f(16, 0, 32, 16, 0, 32, 4, 16, 32, 16, 16, 16, 16, 7, None) == api.EMU_ERR_INVALID_ARG  # profile
+    assert f(16, 0, 32, 16, 0, 32, 0, 16, 32, 0, 16, 0, 16, 0, None) == api.EMU_OK                 # M = 0
+
+
 def test_page_parameters_match_the_library_split_rule():
     """The split layout the library documents is the pages' contiguous rule
     with 128-wide k-tiles (golden page_parameters.json)."""
