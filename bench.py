@@ -18,6 +18,7 @@ against the GPU's output on that sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -122,7 +123,30 @@ def output_bits(t):
     t = t.cpu()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy().astype(np.uint32)
     return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+
+
+def cpu_baseline_incoming(wl, x, w, c_bits, acc_gpu, budget_s: float, profile: str = "hopper"):
+    """The oracle's chains from incoming accumulators, timed on whole output
+    rows sized to about budget_s seconds (one thread: the entry point is not
+    threaded)."""
+    import oracle
+    orc = oracle.default()
+    xs, ws = x.numpy(), w.numpy()
+    t0 = time.perf_counter()
+    orc.accumulate_c(xs[:1], wl.xfmt, ws[:256], wl.wfmt, c_bits[:1, :256], profile=profile)
+    rate = 256 * wl.K / max(time.perf_counter() - t0, 1e-3)
+    rows = int(max(1, min(wl.M, budget_s * rate / (wl.N * wl.K))))
+    t0 = time.perf_counter()
+    acc = orc.accumulate_c(xs[:rows], wl.xfmt, ws, wl.wfmt, c_bits[:rows], profile=profile)
+    dt = time.perf_counter() - t0
+    ops = 2 * rows * wl.N * wl.K
+    return {"value": ops / dt, "unit": "GEMM-ops/s", "cores": 1, "kind": "oracle",
+            "sample": f"output rows 0..{rows - 1} (all {wl.N} columns, K={wl.K}), chains from incoming "
+                      f"accumulators, {ops / 2:.3g} MACs in {dt:.1f} s",
+            "gpu_bit_exact_on_sample": bool(np.array_equal(acc, acc_gpu[:rows]))}
 
 
 def main():
@@ -139,6 +163,10 @@ def main():
                     help="arithmetic profile (hopper is the pages' default)")
     ap.add_argument("--inf-density", type=float, default=0.0, metavar="P",
                     help="replace a fraction P of the e5m2 operand's codes by +-Inf (specials throughput)")
+    ap.add_argument("--out", default=None, choices=sorted(OUT_DTYPES),
+                    help="override the workload's output type (FP8 outputs use scale_result 1)")
+    ap.add_argument("--incoming-acc", action="store_true",
+                    help="time emu_accumulate_c (chains from incoming accumulators) instead of emu_scaled_mm")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -156,6 +184,11 @@ def main():
         sys.exit(2)
 
     wl = WORKLOADS[args.workload]
+    if args.out:
+        wl = dataclasses.replace(wl, out=args.out)
+    if args.incoming_acc and (not wl.fast or wl.split_S != 1):
+        print("bench.py: --incoming-acc needs a fast-accumulation workload with split_S = 1", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     log(f"[bench] generating {wl.name} inputs (seed {args.seed})")
     x, w = make_operands(wl, args.seed)
@@ -190,6 +223,20 @@ def main():
         if st != 0:
             raise api.EmuError(st, lib.emu_last_error_message().decode())
 
+    if args.incoming_acc:
+        # incoming accumulators of a chain's size: N(0, 1) * 2^12, binary32
+        gen = torch.Generator().manual_seed(args.seed + 3000)
+        c_in = (torch.randn((wl.M, wl.N), generator=gen) * 4096.0).to(dev)
+        out = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        cin_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
+                    wl.M, wl.N, wl.K, c_in.data_ptr(), wl.N, out.data_ptr(), wl.N, api.PROFILE[args.profile],
+                    stream.cuda_stream)
+
+        def step():  # noqa: F811 -- the timed call of this mode
+            st = lib.emu_accumulate_c(*cin_args)
+            if st != 0:
+                raise api.EmuError(st, lib.emu_last_error_message().decode())
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -212,7 +259,8 @@ def main():
     value = ops * args.steps / wall
     achieved = ops / (launch_ms * 1e-3)
 
-    traffic = load_traffic(wl.name) if args.inf_density == 0 and args.profile == "hopper" else None
+    default_call = args.inf_density == 0 and args.profile == "hopper" and not args.out and not args.incoming_acc
+    traffic = load_traffic(wl.name) if default_call else None
     result = {
         "metric": METRIC,
         "value": value,
@@ -227,7 +275,8 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": {**wl.describe(), "profile": args.profile, "parallelism": "single GPU",
-                   **({"inf_density": args.inf_density} if args.inf_density > 0 else {})},
+                   **({"inf_density": args.inf_density} if args.inf_density > 0 else {}),
+                   **({"entry_point": "emu_accumulate_c", "out": "fp32 accumulator"} if args.incoming_acc else {})},
         "roofline": {
             "bound": "alu",
             "achieved": achieved / 1e12,
@@ -241,7 +290,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, x, w, output_bits(out), args.cpu_budget, args.profile)
+        if args.incoming_acc:
+            result["cpu_baseline"] = cpu_baseline_incoming(wl, x, w, output_bits(c_in), output_bits(out),
+                                                           args.cpu_budget, args.profile)
+        else:
+            result["cpu_baseline"] = cpu_baseline(wl, x, w, output_bits(out), args.cpu_budget, args.profile)
     print(json.dumps(result), flush=True)
 
 

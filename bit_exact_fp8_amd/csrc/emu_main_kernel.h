@@ -256,6 +256,12 @@ __device__ __forceinline__ uint32_t add_rn(uint32_t a, uint32_t b, uint32_t tok)
     return r;
 }
 
+// c cut toward zero to 14 significant bits from its exponent field (emin for
+// a subnormal c): the low 10 fraction bits cleared.  A negative c that leaves
+// nothing becomes -0, which enters later blocks as +0 does; the chain's end
+// turns it into +0.
+__device__ __forceinline__ uint32_t cut14(uint32_t c) { return c & 0xFFFFFC00u; }
+
 // ---- FP8 decoding -----------------------------------------------------------
 // Four codes of a row (one 32-bit word, k ascending from the low byte) become
 //   four signed binary32 values (exact hardware conversions, subnormals
@@ -777,7 +783,6 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             uint32_t Cb[RM][RN];
             int acc[RM][RN];
             uint32_t reach = 0;  // speculation: bit i*RN+j set if the products alone reach E
-            uint32_t noprod = 0; // incoming accumulators: bit i*RN+j set for a block without products
             if constexpr (MX) {
                 // pass 1 on the matrix cores: per quarter-block, S for every output
                 uint32_t smax[RM][RN];
@@ -810,12 +815,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                             reach |= (gp >= ge ? 1u : 0u) << (i * RN + j);
                             acc[i][j] = 0;
                         } else {
-                            if constexpr (CIN) noprod |= ((smax[i][j] >> 25) == 0u ? 1u : 0u) << (i * RN + j);
                             const uint32_t eb = max((smax[i][j] >> 25) + POW_TO_EB, (c[i][j] >> 23) & 0xFFu);
                             Cb[i][j] = (eb << 23) + C_OFFSET;
                             const uint32_t rc = fma_abs_rz(__uint_as_float(c[i][j]), 1.0f, Cb[i][j], tok);
                             const uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
                             acc[i][j] = dot2_i16_from0(rc, sc);
+                            if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                         }
                     }
             } else {
@@ -880,8 +885,6 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
                         const uint32_t g = gmax[i][j];
-                        if constexpr (CIN)  // zero products' plane sums stay below 0x400 + 88
-                            noprod |= ((max3_lo_hi_u16(g, 0u) & 0x1FFu) < 94u ? 1u : 0u) << (i * RN + j);
                         const uint32_t ec = ((c[i][j] >> 23) & 0xFFu) | SUM_OFFSET;
                         // only the low 9 bits of the maximum reach C
                         Cb[i][j] = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
@@ -890,6 +893,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         uint32_t sc = ((uint32_t)((int)c[i][j] >> 31) & 0xFFFFu) | 1u;
                         if (G > 1) sc = (lane_g == 0) ? sc : 0u;  // c enters the block sum once
                         acc[i][j] = dot2_i16_from0(rc, sc);
+                        if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             }
 
@@ -964,16 +968,16 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         const uint32_t tb = __float_as_uint((float)acc[i][j]) & 0xFFFFFC00u;
                         const uint32_t cn = mul_exact(tb, Cb[i][j] - POW2Q_FROM_C, tok);
                         if constexpr (CIN) {
-                            // A block without products keeps c cut to 14 significant bits
-                            // from its own exponent (emin for a subnormal c), +0 if
-                            // nothing is left: the planes' sentinels sit below 2^-33
-                            // only, and a caller's c can be smaller.  So does any block
-                            // when c >= 2^39: the quantum 2^(E-13) then exceeds every
-                            // product (< 2^25), and C = 1.5 * 2^(E+10) would leave the
-                            // binary32 range for the largest c.
-                            const uint32_t ct = c[i][j] & 0xFFFFFC00u;
-                            const bool alone = ((noprod >> (i * RN + j)) & 1u) || ((c[i][j] >> 23) & 0xFFu) >= 166u;
-                            c[i][j] = alone ? ((ct & 0x7FFFFFFFu) ? ct : 0u) : cn;
+                            // c (cut to 14 significant bits by the prologue) stays when
+                            // the block exponent, biased, is below 94 -- no products
+                            // (their plane sentinels sit at 93 and below) and c under
+                            // 2^-33, where those sentinels would cut it wrongly -- or
+                            // 166 and above -- c >= 2^39, whose quantum 2^(E-13)
+                            // exceeds every product (< 2^25), and where C =
+                            // 1.5 * 2^(E+10) would leave the binary32 range: in both
+                            // cases the block step leaves c cut to 14 significant bits
+                            // biased E in [94, 166) <=> Cb's top bits in [104, 176)
+                            c[i][j] = (Cb[i][j] - (104u << 23) < (72u << 23)) ? cn : c[i][j];
                         } else {
                             c[i][j] = cn;
                         }
@@ -1094,6 +1098,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len, flags[rm] != 0,
                                          flags[BM + rn] != 0);
             if constexpr (CIN) {
+                if (a == 0x80000000u && p.K > 0) a = 0u;  // a zero block result is +0
                 // a NaN c_in gives NaN; an infinite one stays, unless the
                 // products give NaN or the opposite infinity
                 const uint32_t cb = __float_as_uint(p.c_in[m * p.ldc + n]);
