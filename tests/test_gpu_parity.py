@@ -284,6 +284,49 @@ def test_inf_rows_and_columns(dev, orc, profile, S, fast, cfg):
         api.force_tile(prev)
 
 
+# ---- the largest shapes the grid limits allow --------------------------------------------
+@pytest.mark.parametrize("S", [1, 2])
+def test_rows_beyond_one_launch(dev, orc, S):
+    """M above 65535 workgroup rows of the 16-row tile: the host splits the
+    launch into row slices (and, for S = 2, the partials keep one layout);
+    every output against the oracle.  Also the incoming-accumulator entry
+    point over the same rows."""
+    M, N, K = 65535 * 16 + 37, 16, 32
+    gen = torch.Generator().manual_seed(71 + S)
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
+    w = inject(random_codes((N, K), "e5m2", gen), "e5m2", 0.1, 0.05, gen)
+    prev = api.force_tile(8)  # 16x8 tiles, 4 lanes per output
+    try:
+        check(dev, orc, x, "e4m3fn", w, "e5m2", 0.5, 0.25, "bf16", True, S, f"rows beyond one launch S={S}")
+        if S == 1:
+            c = _c_patterns(M, N, np.random.default_rng(3))
+            got = gpu_accumulate_c(dev, x, "e4m3fn", w, "e5m2", c)
+            want = orc.accumulate_c(x.numpy(), "e4m3fn", w.numpy(), "e5m2", c)
+            assert_same(got, want, "incoming accumulators, rows beyond one launch")
+    finally:
+        api.force_tile(prev)
+
+
+@pytest.mark.parametrize("profile", ["hopper", "ada-serial"])
+@pytest.mark.parametrize("fast", [True, False])
+def test_largest_split_count(dev, orc, profile, fast):
+    """split_S = 65535 (the largest grid z) on a K of three k-tiles: every
+    split after the third is empty and adds +0 in the serial combination, so
+    the result must equal the S = 3 one, which the oracle checks."""
+    tile = 128 if profile == "hopper" else 64
+    M, N, K = 20, 32, 3 * tile
+    gen = torch.Generator().manual_seed(73)
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
+    w = inject(random_codes((N, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
+    check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.5, 0.25, "fp32", fast, 3, f"three splits {profile}",
+          profile=profile)
+    y3, acc3 = gpu_run(dev, x, "e4m3fn", w, "e4m3fn", 0.5, 0.25, "fp32", fast, 3, profile=profile)
+    note(f"[gpu] split_S = 65535 {profile} fast={fast}")
+    y, acc = gpu_run(dev, x, "e4m3fn", w, "e4m3fn", 0.5, 0.25, "fp32", fast, 65535, profile=profile)
+    assert_same(acc, acc3, f"split_S = 65535 accumulator {profile}")
+    assert_same(y, y3, f"split_S = 65535 output {profile}")
+
+
 # ---- incoming accumulators -------------------------------------------------------------
 C_CRAFTED = [0, 0x80000000, 1, 0x80000001, 0x3FF, 0x400, 0x7FFFFF, 0x807FFFFF, 0x800000, 0x00FFFFFF,
              0x3F7FFFFF, 0xBF7FFFFF, 0x3F800001, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F800000, 0xFF800000,
