@@ -69,6 +69,8 @@ def _lib():
     lib.emu_debug_force_tile.restype = i32
     lib.emu_debug_force_spec.argtypes = [i32]
     lib.emu_debug_force_spec.restype = i32
+    lib.emu_debug_force_defer.argtypes = [i32]
+    lib.emu_debug_force_defer.restype = i32
     _LIB = lib
     return lib
 
@@ -100,6 +102,19 @@ def force_spec(mode: str) -> str:
     if prev == -2:
         raise ValueError(f"invalid speculation mode {mode}")
     return {v: k for k, v in SPEC_MODES.items()}[prev]
+
+
+DEFER_MODES = {"auto": -1, "off": 0, "on": 1}
+
+
+def force_defer(mode: str) -> str:
+    """Force the deferred-infinity plan (a key of DEFER_MODES: automatic from
+    2^36 multiply-adds, never, or at every size the plan allows).  Returns the
+    previous mode's name."""
+    prev = _lib().emu_debug_force_defer(DEFER_MODES[mode])
+    if prev == -2:
+        raise ValueError(f"invalid deferred-infinity mode {mode}")
+    return {v: k for k, v in DEFER_MODES.items()}[prev]
 
 
 def _check(status: int):

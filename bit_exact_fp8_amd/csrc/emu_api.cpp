@@ -59,8 +59,12 @@ struct Plan {
     int spec_cfg;
     int64_t nbs;
     int guess_perturb;
+    // infinities resolved after the main kernel (see make_plan)
+    int defer;
     // workspace layout: [split partials][range-start guesses][block words]
-    int64_t part_bytes, guess_bytes, pk_bytes;
+    // [infinity lists]; the first three are required, the lists optional
+    int64_t part_bytes, guess_bytes, pk_bytes, defer_bytes;
+    int64_t required_bytes() const { return part_bytes + guess_bytes + pk_bytes; }
 };
 
 constexpr int64_t kChunk = 128;                          // slow-accumulation restart
@@ -68,9 +72,13 @@ constexpr int64_t kChunkWaveTarget = 4096;               // 4 waves on each SIMD
 constexpr int64_t kMaxChunkWorkspace = int64_t(1) << 30; // bytes of stored chunk results
 constexpr int64_t kResidentWgs = 256 * 3;                // 64x64 workgroups resident at once
 constexpr int64_t kMaxSpecWorkspace = int64_t(1) << 31;  // bytes of block words
+constexpr double kDeferMinWork = 68719476736.0;          // M * N * K = 2^36
+constexpr int64_t kDeferMaxK = emu::kDeferLdsBytes - 16; // one staged B row fits
 
 // Exponent speculation forced through emu_debug_force_spec (-1: automatic).
 std::atomic<int> g_forced_spec{-1};
+// Deferred infinities forced through emu_debug_force_defer (-1: automatic).
+std::atomic<int> g_forced_defer{-1};
 // Tile configuration forced through emu_debug_force_tile (-1: automatic).
 std::atomic<int> g_forced_tile{-1};
 
@@ -191,6 +199,26 @@ Plan make_plan(emu_profile profile, int64_t M, int64_t N, int64_t K, int S, int 
             p.guess_bytes = (int64_t)S * p.chunk_groups * M * N * 4;
             p.pk_bytes = pk_bytes;
         }
+    }
+    // An output whose e5m2 row holds an infinity is non-finite whatever the
+    // chain computes; in the main kernel each such output reads its rows
+    // once more, which on large problems with infinities in many rows can
+    // double the run time (8192^3 with one e5m2 code in 1,000 infinite:
+    // 88.8 ms against 45.0 ms).  On problems of 2^36 multiply-adds and more
+    // the main kernel leaves those outputs alone; a pass over the e5m2 rows
+    // lists their infinities (about 10 us per 64 MiB of codes, the only cost
+    // when there are none) and a fix-up kernel resolves each affected output
+    // from the lists.  The lists take (kDeferCap + 1) 32-bit words per row of
+    // the larger operand, from the optional end of the workspace; stored
+    // chunk results and speculation keep the main kernel's own handling.
+    p.defer = 0;
+    p.defer_bytes = 0;
+    const int forced_defer = g_forced_defer.load(std::memory_order_relaxed);
+    const bool big = (double)M * (double)N * (double)K >= kDeferMinWork;
+    if (!p.chunked && !p.spec && M > 0 && N > 0 && K > 0 && K <= kDeferMaxK && forced_defer != 0 &&
+        (big || forced_defer == 1)) {
+        p.defer = 1;
+        p.defer_bytes = (M > N ? M : N) * (int64_t)(emu::kDeferCap + 1) * 4;
     }
     return p;
 }
@@ -365,6 +393,40 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
     p.scale_w = sw;
     p.scale_result = sr;
     p.w = w;
+    // deferred infinities: only where a format has them and the workspace
+    // holds the lists
+    const int64_t required = plan.required_bytes();
+    emu::DeferParams d{};
+    const bool defer = plan.defer && (xf == EMU_FP8_E5M2 || wf == EMU_FP8_E5M2) && workspace &&
+                       (reinterpret_cast<uintptr_t>(workspace) & 3u) == 0 &&
+                       (int64_t)workspace_bytes >= required + plan.defer_bytes;
+    if (defer) {
+        const bool a_is_w = wf == EMU_FP8_E5M2;
+        d.a = a_is_w ? w : x;
+        d.lda = a_is_w ? ldw : ldx;
+        d.b = a_is_w ? x : w;
+        d.ldb = a_is_w ? ldx : ldw;
+        d.ra = (int)(a_is_w ? N : M);
+        d.rb = (int)(a_is_w ? M : N);
+        d.K = K;
+        d.a_is_w = a_is_w ? 1 : 0;
+        d.info = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + required);
+        d.pos = d.info + (M > N ? M : N);
+        const int64_t br = emu::kDeferLdsBytes / (K + 16);
+        d.b_rows = (int)(br < 16 ? br : 16);
+        const int64_t ar = (d.ra + kMaxGridY - 1) / kMaxGridY;
+        d.a_rows = (int)(ar > 2048 ? ar : 2048);
+        d.out_kind = out_kind;
+        d.out = out;
+        d.ldo = ldo;
+        d.scale_x = sx;
+        d.scale_w = sw;
+        d.scale_result = sr;
+        hipError_t e = emu::launch_inf_rows(d, stream);
+        if (e != hipSuccess)
+            return fail(EMU_ERR_DEVICE, std::string("infinity row kernel launch: ") + hipGetErrorString(e));
+        p.defer_specials = 1;
+    }
     if (!partials) {
         p.out_kind = out_kind;
         p.ldo = ldo;
@@ -390,7 +452,11 @@ emu_status run(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const uint8_t *
                                           sx, sw, sr, stream);
         if (st != EMU_OK) return st;
     }
-    (void)workspace_bytes;
+    if (defer) {
+        hipError_t e = emu::launch_inf_fixup(d, stream);
+        if (e != hipSuccess)
+            return fail(EMU_ERR_DEVICE, std::string("infinity fix-up kernel launch: ") + hipGetErrorString(e));
+    }
     return ok();
 }
 
@@ -402,7 +468,7 @@ size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fas
 {
     if (M < 0 || N < 0 || K < 0 || split_S < 1 || split_S > kMaxSplits) return 0;
     const Plan plan = make_plan(profile, M, N, K, split_S, fast_accum);
-    return (size_t)(plan.part_bytes + plan.guess_bytes + plan.pk_bytes);
+    return (size_t)(plan.required_bytes() + plan.defer_bytes);
 }
 
 emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
@@ -431,9 +497,9 @@ emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, co
     if (M == 0 || N == 0) return ok();
     if (!out || !scale_x || !scale_w) return fail(EMU_ERR_INVALID_ARG, "null output or scale pointer");
     if (!aligned16(out)) return fail(EMU_ERR_REJECTED, "out must be 16-byte aligned");
-    const size_t need = emu_workspace_bytes(M, N, K, split_S, fast_accum, profile);
+    const size_t need = (size_t)make_plan(profile, M, N, K, split_S, fast_accum).required_bytes();
     if (workspace_bytes < need || (need && !workspace))
-        return fail(EMU_ERR_WORKSPACE, "workspace smaller than emu_workspace_bytes()");
+        return fail(EMU_ERR_WORKSPACE, "workspace smaller than the split partials need");
     if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
         return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
     return run(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, scale_x, scale_w, scale_result, out, kind, elem, ldo,
@@ -451,9 +517,9 @@ emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, c
     if (M == 0 || N == 0) return ok();
     if (!acc) return fail(EMU_ERR_INVALID_ARG, "null accumulator pointer");
     if (reinterpret_cast<uintptr_t>(acc) & 3u) return fail(EMU_ERR_INVALID_ARG, "acc must be 4-byte aligned");
-    const size_t need = emu_workspace_bytes(M, N, K, split_S, fast_accum, profile);
+    const size_t need = (size_t)make_plan(profile, M, N, K, split_S, fast_accum).required_bytes();
     if (workspace_bytes < need || (need && !workspace))
-        return fail(EMU_ERR_WORKSPACE, "workspace smaller than emu_workspace_bytes()");
+        return fail(EMU_ERR_WORKSPACE, "workspace smaller than the split partials need");
     if (need && (reinterpret_cast<uintptr_t>(workspace) & 3u))
         return fail(EMU_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
     // The scale pointers are not read for the accumulator.
@@ -533,6 +599,12 @@ int emu_debug_force_spec(int mode)
 {
     if (mode < -1 || mode > 3) return -2;
     return g_forced_spec.exchange(mode);
+}
+
+int emu_debug_force_defer(int mode)
+{
+    if (mode < -1 || mode > 1) return -2;
+    return g_forced_defer.exchange(mode);
 }
 
 uint32_t emu_host_mul_f32(uint32_t a, uint32_t b) { return emu::mul_f32(a, b); }

@@ -61,6 +61,38 @@ struct MainParams {
     // from c_in[m * ldc + n] instead of +0.
     const float *c_in;
     int64_t ldc;
+    // 1: outputs whose rows hold infinities (and no NaN) are left as the
+    // chain computed them; the infinity fix-up kernel overwrites them.
+    int defer_specials;
+};
+
+// Deferred infinities.  Operand A is the e5m2 one (the only format with
+// infinities; the other, B, is e4m3fn).  The row kernel writes, for each A
+// row, info[a] = the number of infinity codes in it, or 0 when there is none
+// or the row holds a NaN code (the main kernel resolves NaN rows itself), and
+// the positions k | sign << 31 of the first kDeferCap of them, in any order,
+// to pos[a * kDeferCap + i].  The fix-up kernel overwrites every output whose
+// A row has info != 0 and whose B row holds no NaN code with the specials
+// rule's result, read from those lists and the B row (staged in LDS), or
+// from the whole A row where a list overflowed.
+constexpr int kDeferCap = 64;
+constexpr int64_t kDeferLdsBytes = 63 * 1024;  // staged B rows per fix-up workgroup, at most
+
+struct DeferParams {
+    const uint8_t *a, *b;  // A and B rows, strides lda, ldb bytes
+    int64_t lda, ldb;
+    int ra, rb;            // A and B rows
+    int64_t K;
+    int a_is_w;            // 1: output (m, n) = (B row, A row); 0: (A row, B row)
+    uint32_t *info;        // [ra]
+    uint32_t *pos;         // [ra * kDeferCap]
+    int b_rows;            // B rows staged per fix-up workgroup (1..16, row stride K + 16 bytes)
+    int a_rows;            // A rows per fix-up workgroup
+    int out_kind;          // OUT_ACC_F32 or an epilogue kind
+    void *out;             // [M, N], row stride ldo elements
+    int64_t ldo;
+    const float *scale_x, *scale_w;
+    const float *scale_result;
 };
 
 struct CombineParams {
@@ -118,5 +150,9 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream);
 // The main kernel from incoming accumulators (grid z = 1).
 hipError_t launch_main_cin(int cfg, int block, int xfmt, int wfmt, const MainParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
+// The infinity row kernel, then (after the main and combine kernels) the
+// fix-up kernel.
+hipError_t launch_inf_rows(const DeferParams &p, hipStream_t stream);
+hipError_t launch_inf_fixup(const DeferParams &p, hipStream_t stream);
 
 }  // namespace emu

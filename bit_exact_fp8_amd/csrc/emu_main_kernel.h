@@ -1094,7 +1094,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             uint32_t a = FAST ? c[i][j] : slow[RUNNING ? i : 0][RUNNING ? j : 0];
             const uint32_t f = flags[rm] | flags[BM + rn];
             if (f & 2u) a = kCanonNan32;  // a NaN code in either row wins
-            else if (f)  // infinities
+            else if (f && !p.defer_specials)  // infinities (or left to the fix-up kernel)
                 a = special_scan<XF, WF>(p.x + m * p.ldx, p.w + n * p.ldw, sq, 0, sq.len, flags[rm] != 0,
                                          flags[BM + rn] != 0);
             if constexpr (CIN) {

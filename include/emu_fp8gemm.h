@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define EMU_ABI_VERSION 3
+#define EMU_ABI_VERSION 4
 
 #if defined(EMU_BUILDING_LIBRARY)
 #define EMU_API __attribute__((visibility("default")))
@@ -78,7 +78,7 @@ typedef enum {
                                 ldx or ldw not a multiple of 16 */
     EMU_ERR_UNSUPPORTED = 3, /* a feature outside this library: split_S above 65535, M or N above 2^31-1,
                                 scale_result with a non-FP8 output */
-    EMU_ERR_WORKSPACE = 4,   /* workspace_bytes < emu_workspace_bytes(...) */
+    EMU_ERR_WORKSPACE = 4,   /* workspace smaller than the required part of emu_workspace_bytes(...) */
     EMU_ERR_DEVICE = 5       /* a HIP launch or runtime error */
 } emu_status;
 
@@ -128,9 +128,13 @@ typedef enum {
  *
  * M >= 0 (any value), N >= 0 and K >= 0 multiples of 16.  M = 0 or N = 0
  * returns EMU_OK without enqueuing anything; K = 0 writes +0 everywhere.
- * workspace: device memory of at least emu_workspace_bytes(M, N, K, split_S,
- * fast_accum, profile) bytes (may be NULL when that is 0); its contents on
- * entry do not matter.  stream: a hipStream_t (NULL = the default stream).
+ * workspace: device memory of emu_workspace_bytes(M, N, K, split_S,
+ * fast_accum, profile) bytes (may be NULL when that is 0), 4-byte aligned;
+ * its contents on entry do not matter.  Only the split partials, stored
+ * chunk results and speculation arrays are required (a smaller workspace
+ * returns EMU_ERR_WORKSPACE); without the optional infinity lists at its end
+ * the call is still bit-exact, only slower on large inputs whose e5m2 rows
+ * hold infinities.  stream: a hipStream_t (NULL = the default stream).
  */
 EMU_API emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
                          const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
@@ -178,13 +182,19 @@ EMU_API emu_status emu_accumulate_c(const uint8_t *x, emu_fp8_format x_fmt, int6
                                     const float *c_in, int64_t ldc, float *acc, int64_t ldacc,
                                     emu_profile profile, void *stream);
 
-/* Device workspace in bytes that emu_scaled_mm and emu_accumulate need for these
- * arguments (0 for invalid sizes): split partials (split_S * M * N * 4 when
- * split_S > 1), the results of groups of 128-K chunks when slow accumulation
- * over a small output grid stores them, or, for fast accumulation over a
- * small output grid with long chains, the exponent-speculation arrays (one
- * 4-byte word per 32 or 16 products of every output, plus one guess per
- * output and K range).  Depends on the plan only, never on the data. */
+/* Device workspace in bytes for emu_scaled_mm and emu_accumulate with these
+ * arguments (0 for invalid sizes).  Required: split partials
+ * (split_S * M * N * 4 when split_S > 1), the results of groups of 128-K
+ * chunks when slow accumulation over a small output grid stores them, or,
+ * for fast accumulation over a small output grid with long chains (when
+ * forced), the exponent-speculation arrays (one 4-byte word per 32 or 16
+ * products of every output, plus one guess per output and K range).
+ * Optional, at the end: on problems of M * N * K >= 2^36 with K <= 64496
+ * that store no chunk results, the infinity lists, 65 * 4 bytes per row of
+ * the larger of M and N (e5m2 operands only use them): a pass over the e5m2
+ * operand lists where each row holds infinities, the main kernel skips the
+ * outputs those rows make non-finite, and a fix-up kernel resolves them from
+ * the lists.  Depends on the plan only, never on the data or formats. */
 EMU_API size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum,
                            emu_profile profile);
 
@@ -223,6 +233,16 @@ EMU_API int emu_debug_force_tile(int cfg);
  * emu_debug_force_tile.
  */
 EMU_API int emu_debug_force_spec(int mode);
+
+/*
+ * Testing and tuning: force the deferred-infinity plan described at
+ * emu_workspace_bytes (mode -1: automatic, from 2^36 multiply-adds; 0:
+ * never; 1: at every size the plan allows).  Results do not depend on the
+ * mode.  The mode also changes emu_workspace_bytes.  Returns the previous
+ * mode, or -2 (and changes nothing) for an invalid mode.  Process-wide, like
+ * emu_debug_force_tile.
+ */
+EMU_API int emu_debug_force_defer(int mode);
 
 /*
  * Host builds of the library's own IEEE rounding routines, the same source

@@ -47,7 +47,7 @@ def test_abi_version(lib):
     """The library reports the EMU_ABI_VERSION of the header it was built with."""
     hdr = open(os.path.join(ROOT, "include", "emu_fp8gemm.h")).read()
     want = int(hdr.split("#define EMU_ABI_VERSION")[1].split()[0])
-    assert api.abi_version() == want == 3
+    assert api.abi_version() == want == 4
 
 
 def test_status_strings(lib):
@@ -58,8 +58,52 @@ def test_status_strings(lib):
 def test_workspace_bytes():
     assert api.workspace_bytes(16, 256, 65536, 8) == 8 * 16 * 256 * 4
     assert api.workspace_bytes(64, 5760, 1920, 1) == 0
-    assert api.workspace_bytes(8192, 8192, 8192, 1) == 0
+    assert api.workspace_bytes(8192, 8192, 8192, 1) == 8192 * 65 * 4   # the optional infinity lists
     assert api._lib().emu_workspace_bytes(-1, 16, 16, 2, 1, 0) == 0
+
+
+# the optional infinity lists: 64 positions and a count per row of the larger operand
+LISTS = 65 * 4
+
+
+@pytest.mark.parametrize("M,N,K,S,fast,profile,auto,forced", [
+    (8192, 8192, 8192, 1, True, "hopper", 8192, 8192),            # 2^39 multiply-adds
+    (4096, 4096, 4096, 1, True, "hopper", 4096, 4096),            # 2^36: the threshold
+    (4096, 4096, 4080, 1, True, "hopper", 0, 4096),               # just below it
+    (64, 5760, 1920, 1, True, "hopper", 0, 5760),
+    (8192, 8192, 8192, 3, True, "ada-pairwise", 8192, 8192),      # with split partials
+    (8192, 8192, 8192, 1, False, "hopper", 8192, 8192),           # slow, enough tiles: no stored chunks
+    (256, 4096, 4096, 1, False, "hopper", 0, 0),                  # slow with stored chunk results: never
+    (16, 256, 65536, 8, True, "hopper", 0, 0),                    # K above one staged row of LDS
+    (16, 256, 64496, 1, True, "hopper", 0, 256),                  # the largest K that fits
+    (16, 256, 64512, 1, True, "hopper", 0, 0),
+])
+def test_workspace_for_deferred_infinities(M, N, K, S, fast, profile, auto, forced):
+    """The infinity lists are planned from 2^36 multiply-adds (or at every
+    size when forced), for K up to 64,496, never with stored chunk results;
+    they are the optional last part of the workspace."""
+    prev = api.force_defer("off")
+    try:
+        base = api.workspace_bytes(M, N, K, S, fast, profile)
+        api.force_defer("auto")
+        assert api.workspace_bytes(M, N, K, S, fast, profile) == base + auto * LISTS
+        api.force_defer("on")
+        assert api.workspace_bytes(M, N, K, S, fast, profile) == base + forced * LISTS
+    finally:
+        api.force_defer(prev)
+
+
+def test_force_defer(lib):
+    """The deferred-infinity modes are accepted and returned; others are
+    refused without changing the setting."""
+    prev = api.force_defer("auto")
+    try:
+        assert api.force_defer("on") == "auto"
+        assert api.force_defer("off") == "on"
+        assert lib.emu_debug_force_defer(2) == -2 and lib.emu_debug_force_defer(-2) == -2
+        assert api.force_defer("auto") == "off"
+    finally:
+        api.force_defer(prev)
 
 
 @pytest.mark.parametrize("M,N,K,S,profile,block", [(16, 256, 65536, 8, "hopper", 32), (64, 5760, 1920, 1, "hopper", 32),
@@ -299,7 +343,7 @@ def test_workspace_for_chunked_slow_accumulation(lib):
     kernel; large grids need no such array."""
     assert api.workspace_bytes(256, 4096, 4096, 1, False) == 32 * 256 * 4096 * 4
     assert api.workspace_bytes(256, 4096, 4096, 1, True) == 0
-    assert api.workspace_bytes(8192, 8192, 8192, 1, False) == 0       # enough tiles already
+    assert api.workspace_bytes(8192, 8192, 8192, 1, False) == 8192 * 65 * 4  # enough tiles: lists only
     assert api.workspace_bytes(16, 256, 65536, 8, False) == 8 * 64 * 16 * 256 * 4
     assert api.workspace_bytes(64, 64, 128, 1, False) == 0            # a single chunk
     # ada: 64-wide tiles dealt round-robin; the longest split sets the chunk count

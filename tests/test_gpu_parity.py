@@ -284,6 +284,113 @@ def test_inf_rows_and_columns(dev, orc, profile, S, fast, cfg):
         api.force_tile(prev)
 
 
+# ---- infinities resolved after the main kernel --------------------------------------------
+def _listed_infinities(e5, rng):
+    """Rows with 63, 64 and 65 infinities around the per-row list's capacity
+    of 64 (row 9: 64 of both signs, row 10: 65 negative ones, past the
+    capacity, rows 11 and 12: 63 and 64 positive ones)."""
+    K = e5.shape[1]
+    for r, count, codes in ((9, 64, [0x7C, 0xFC]), (10, 65, [0xFC]), (11, 63, [0x7C]), (12, 64, [0x7C])):
+        row = e5[r, :] & 0x7F
+        row[row == 0x7C] = 0x3C                                      # no infinities but the listed ones
+        row[row > 0x7C] = 0x3C
+        ks = rng.choice(K, count, replace=False)
+        row[ks] = torch.from_numpy(rng.choice(codes, count).astype(np.uint8))
+        e5[r, :] = row
+
+
+def _deferred_operands(e5_is_x, e5_rows, other_rows, K, seed):
+    e5, ot = _inf_rows_and_columns(e5_rows, other_rows, K, seed)
+    _listed_infinities(e5, np.random.default_rng(seed + 1))
+    if e5_is_x:
+        return e5, "e5m2", ot, "e4m3fn"
+    return ot, "e4m3fn", e5, "e5m2"
+
+
+@pytest.mark.parametrize("profile,S,fast,K", [("hopper", 1, True, 1040), ("hopper", 3, True, 1040),
+                                              ("ada-pairwise", 5, True, 1040), ("ada-serial", 2, False, 1040),
+                                              ("hopper", 1, True, 64496), ("ada-serial", 1, True, 64496)])
+def test_deferred_infinities(dev, orc, profile, S, fast, K):
+    """The deferred-infinity plan forced on small shapes: the row pass lists
+    each e5m2 row's infinities and the fix-up kernel resolves the outputs
+    those rows make non-finite (whole rows of infinities and rows past the
+    list's capacity through the row walk; NaN rows in either operand left to
+    the main kernel; a partial last block of staged rows), on both operands,
+    against the oracle; with negative and zero scales (the epilogue's sign
+    and Inf * 0), every output kind, and K = 64,496, the largest K whose
+    rows fit the fix-up's LDS.  Small slow-mode grids store chunk results and
+    keep the main kernel's own handling."""
+    prev = api.force_defer("on")
+    try:
+        for e5_is_x in (True, False):
+            x, xfmt, w, wfmt = _deferred_operands(e5_is_x, 44 if e5_is_x else 48, 48 if e5_is_x else 44, K,
+                                                  21 + S + K)
+            if K > 2048:
+                check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", fast, S,
+                      f"deferred infinities {xfmt}x{wfmt} K={K}", profile=profile)
+                continue
+            for out, sx in (("bf16", 0.1), ("fp32", -0.1), ("e5m2", 0.0), ("fp16", 2.0), ("e4m3fn", 0.1)):
+                check(dev, orc, x, xfmt, w, wfmt, sx, 1 / 3, out, fast, S,
+                      f"deferred infinities {xfmt}x{wfmt} out={out} sx={sx}", profile=profile)
+    finally:
+        api.force_defer(prev)
+
+
+def test_deferred_infinities_slow_grid(dev, orc):
+    """Slow accumulation on a grid large enough that no chunk results are
+    stored (2304 x 2304 x 1040), so the deferred plan applies, with two
+    groups of 2,048 e5m2 rows in the fix-up grid; every output against the
+    oracle."""
+    prev = api.force_defer("on")
+    try:
+        x, xfmt, w, wfmt = _deferred_operands(False, 2304, 2304, 1040, 31)
+        assert api.workspace_bytes(2304, 2304, 1040, 1, False) == 2304 * 65 * 4   # lists, no chunk results
+        check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", False, 1, "deferred infinities, slow grid")
+    finally:
+        api.force_defer(prev)
+
+
+def test_deferred_infinities_workload(dev, orc):
+    """The 8192^3 e4m3fn x e5m2 workload with one w code in 1,000 an
+    infinity (random signs), some w rows with 64, 65 or K infinities and a
+    few NaN rows in both operands: the automatic plan defers the infinities
+    (2^39 multiply-adds); every output must equal the main kernel's own
+    handling (deferral forced off), and sampled outputs, a third of them in
+    NaN or infinity rows, the oracle's."""
+    wl = WORKLOADS["mixed_8192"]
+    x, w = make_operands(wl, 0)
+    gen = torch.Generator().manual_seed(2000)
+    hit = torch.rand(w.shape, generator=gen) < 1e-3
+    signs = torch.randint(0, 2, w.shape, generator=gen, dtype=torch.uint8) << 7
+    w[hit] = signs[hit] | 0x7C
+    rng = np.random.default_rng(5)
+    w[100, :] = 0x7C
+    _listed_infinities(w[200:213], rng)
+    w[300, 4000] = 0x7E                                              # e5m2 NaN
+    x[400, 17] = 0xFF                                                # e4m3fn NaN
+    assert api.workspace_bytes(wl.M, wl.N, wl.K, 1, True) == wl.N * 65 * 4
+    note("[gpu] mixed_8192 with infinities: deferred (automatic)")
+    y, acc = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S)
+    prev = api.force_defer("off")
+    try:
+        note("[gpu] mixed_8192 with infinities: in the main kernel")
+        y0, acc0 = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S)
+    finally:
+        api.force_defer(prev)
+    assert_same(acc, acc0, "deferred vs in-kernel infinities, accumulator")
+    assert_same(y, y0, "deferred vs in-kernel infinities, output")
+    ms = list(rng.integers(0, wl.M, 1500)) + [400] * 20 + list(rng.integers(0, wl.M, 60))
+    ns = list(rng.integers(0, wl.N, 1500)) + list(rng.integers(0, wl.N, 20)) + \
+        [100] * 10 + [300] * 10 + list(range(200, 213)) * 3 + [209]
+    ms, ns = np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+    acc_o, y_o = orc.points(x.numpy(), wl.xfmt, w.numpy(), wl.wfmt, ms, ns, scale_bits(wl.scale_x),
+                            scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S)
+    assert_same(acc[ms, ns], acc_o, "mixed_8192 with infinities, accumulator")
+    assert_same(y[ms, ns], y_o, "mixed_8192 with infinities, output")
+    nonfinite = int(((acc_o & 0x7F800000) == 0x7F800000).sum())
+    assert nonfinite > 500, nonfinite
+
+
 # ---- the largest shapes the grid limits allow --------------------------------------------
 @pytest.mark.parametrize("S", [1, 2])
 def test_rows_beyond_one_launch(dev, orc, S):
