@@ -336,6 +336,36 @@ def test_deferred_infinities(dev, orc, profile, S, fast, K):
         api.force_defer(prev)
 
 
+def test_deferred_infinities_strided(dev, orc):
+    """The deferred plan on operands whose rows are longer than K (ldx, ldw
+    > K) and an output whose rows are longer than N (ldo > N), with the e5m2
+    operand on either side; the padding of the output rows stays untouched."""
+    K, pad = 1040, 64
+    prev = api.force_defer("on")
+    try:
+        for e5_is_x in (True, False):
+            x, xfmt, w, wfmt = _deferred_operands(e5_is_x, 44 if e5_is_x else 48, 48 if e5_is_x else 44, K, 41)
+            M, N = x.shape[0], w.shape[0]
+            xw = torch.zeros((M, K + pad), dtype=torch.uint8)
+            ww = torch.zeros((N, K + pad), dtype=torch.uint8)
+            xw[:, :K], ww[:, :K] = x, w
+            xw[:, K:], ww[:, K:] = 0x7C if e5_is_x else 0x7F, 0x7F if e5_is_x else 0x7C  # specials past K
+            xd = xw.to(dev)[:, :K].view(FP8_DTYPES[xfmt])
+            wd = ww.to(dev)[:, :K].view(FP8_DTYPES[wfmt])
+            ob = torch.full((M, N + 16), -7.0, dtype=torch.bfloat16, device=dev)
+            o = ob[:, :N]
+            sx = torch.tensor([0.1], device=dev)
+            sw = torch.tensor([1 / 3], device=dev)
+            note(f"[gpu] deferred infinities strided {xfmt}x{wfmt}")
+            api.scaled_mm(xd, wd.t(), sx, sw, out_dtype=torch.bfloat16, use_fast_accum=True, out=o)
+            torch.cuda.synchronize(dev)
+            _, y_o = oracle_run(orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", True, 1)
+            assert_same(bits_of(o.contiguous()), y_o, f"deferred infinities strided {xfmt}x{wfmt}")
+            assert bool((ob[:, N:] == -7.0).all()), "output padding written"
+    finally:
+        api.force_defer(prev)
+
+
 def test_deferred_infinities_slow_grid(dev, orc):
     """Slow accumulation on a grid large enough that no chunk results are
     stored (2304 x 2304 x 1040), so the deferred plan applies, with two
