@@ -16,7 +16,10 @@ namespace {
 // (for h = P/2 .. 1: p_i += p_{i+h} where i + h < S; S = 3 gives
 // (p0 + p2) + p1).  That tree is the tree of adjacent pairs over the leaves
 // in bit-reversed index order, evaluated here left to right with one pending
-// left operand per level; leaves at index >= S are absent.
+// left operand per level; leaves at index >= S are absent.  CHUNKED: the
+// partials are slow-mode chunk results, cps per split (a separate kernel, so
+// that the one-partial-per-split case keeps its own simpler code).
+template <bool CHUNKED>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -25,13 +28,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     const int64_t m = idx / p.N, n = idx - m * p.N;
     // split s's partial: its single partial, or the running binary32 sum of
     // its slow-mode chunk results in order from +0 (chunk results are never
-    // -0, so the first add reproduces the first chunk bit for bit)
+    // -0, so the first add reproduces the first chunk bit for bit).  Eight
+    // loads are issued before their adds, which stay in order.
+    constexpr int U = 8;
+    auto ordered_sum = [&](const float *q, int n, int64_t stride, float a) {
+        int c = 0;
+        for (; c + U <= n; c += U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = q[(int64_t)(c + u) * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u) a = a + v[u];
+        }
+        for (; c < n; ++c) a = a + q[(int64_t)c * stride];
+        return a;
+    };
     auto split_partial = [&](int s) {
         const float *q = p.part + (int64_t)s * p.cps * total + idx;
-        if (p.cps == 1) return q[0];
-        float a = 0.0f;
-        for (int c = 0; c < p.cps; ++c) a = a + q[(int64_t)c * total];
-        return a;
+        if (!CHUNKED) return q[0];
+        return ordered_sum(q, p.cps, total, 0.0f);
     };
     float acc;
     if (!p.pairwise) {
@@ -131,7 +146,10 @@ hipError_t launch_combine(const CombineParams &p, hipStream_t stream)
 {
     const int64_t total = (int64_t)p.M * p.N;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    if (p.cps > 1)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

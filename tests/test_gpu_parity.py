@@ -366,16 +366,20 @@ def test_deferred_infinities_strided(dev, orc):
         api.force_defer(prev)
 
 
-def test_deferred_infinities_slow_grid(dev, orc):
+@pytest.mark.parametrize("MN,S,profile", [(2304, 1, "hopper"), (1440, 2, "ada-serial")])
+def test_deferred_infinities_slow_grid(dev, orc, MN, S, profile):
     """Slow accumulation on a grid large enough that no chunk results are
-    stored (2304 x 2304 x 1040), so the deferred plan applies, with two
-    groups of 2,048 e5m2 rows in the fix-up grid; every output against the
-    oracle."""
+    stored (2304 x 2304 x 1040, or 1440 x 1440 x 1040 in two splits), so the
+    deferred plan applies (with two groups of 2,048 e5m2 rows in the fix-up
+    grid at 2304, after the combine kernel at S = 2); every output against
+    the oracle."""
     prev = api.force_defer("on")
     try:
-        x, xfmt, w, wfmt = _deferred_operands(False, 2304, 2304, 1040, 31)
-        assert api.workspace_bytes(2304, 2304, 1040, 1, False) == 2304 * 65 * 4   # lists, no chunk results
-        check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", False, 1, "deferred infinities, slow grid")
+        x, xfmt, w, wfmt = _deferred_operands(False, MN, MN, 1040, 31 + S)
+        part = S * MN * MN * 4 if S > 1 else 0
+        assert api.workspace_bytes(MN, MN, 1040, S, False, profile) == part + MN * 65 * 4  # lists, no chunks
+        check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", False, S, f"deferred infinities, slow grid S={S}",
+              profile=profile)
     finally:
         api.force_defer(prev)
 
