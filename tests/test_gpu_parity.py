@@ -336,6 +336,27 @@ def test_deferred_infinities(dev, orc, profile, S, fast, K):
         api.force_defer(prev)
 
 
+@pytest.mark.parametrize("cfg", range(len(api.TILE_CONFIGS)))
+def test_deferred_infinities_every_tile(dev, orc, cfg):
+    """The deferred plan with every tile configuration of the main kernel
+    (each skips its own infinity scan for the fix-up to resolve), fast
+    accumulation in one and in three splits, the e5m2 operand on either
+    side."""
+    K = 528
+    prev_d = api.force_defer("on")
+    prev_t = api.force_tile(cfg)
+    try:
+        for e5_is_x in (True, False):
+            x, xfmt, w, wfmt = _deferred_operands(e5_is_x, 36 if e5_is_x else 48, 48 if e5_is_x else 36, K,
+                                                  51 + cfg)
+            for S in (1, 3):
+                check(dev, orc, x, xfmt, w, wfmt, 0.1, 1 / 3, "bf16", True, S,
+                      f"deferred infinities tile {api.TILE_CONFIGS[cfg]} {xfmt}x{wfmt} S={S}")
+    finally:
+        api.force_tile(prev_t)
+        api.force_defer(prev_d)
+
+
 def test_deferred_infinities_strided(dev, orc):
     """The deferred plan on operands whose rows are longer than K (ldx, ldw
     > K) and an output whose rows are longer than N (ldo > N), with the e5m2
