@@ -63,6 +63,9 @@
 #define MUT_SR_FOLDED         21  /* scale_result folded into alpha instead of a separate multiply */
 #define MUT_FP8_NO_SATURATION 22  /* FP8 outputs overflow to NaN / Inf instead of saturating */
 #define MUT_C_OWN_EXPONENT    23  /* a binary32 subnormal c aligned at floor(log2|c|), not emin */
+#define MUT_INF_TIMES_ZERO    24  /* an infinity times a zero taken as that infinity, not NaN */
+#define MUT_INF_FIRST_SIGN    25  /* infinite products of both signs give the first one's sign */
+#define MUT_C_INF_ABSORBS     26  /* an infinite c_in stays even against the opposite infinity */
 
 /* ------------------------------------------------------------------------ */
 /* Public constants (mirrored in oracle/__init__.py).                        */
@@ -544,7 +547,12 @@ static int special_class(const operands *o, int64_t m, int64_t n, int *neg)
         fp8_val b = decode_fp8(w_at(o, n, k), o->wfmt);
         if (a.cls == CLS_NAN || b.cls == CLS_NAN) { nan = 1; continue; }
         if (a.cls == CLS_INF || b.cls == CLS_INF) {
+#if ORACLE_MUTANT != MUT_INF_TIMES_ZERO
             if (a.cls == CLS_ZERO || b.cls == CLS_ZERO) { nan = 1; continue; }
+#endif
+#if ORACLE_MUTANT == MUT_INF_FIRST_SIGN
+            if (pos_inf || neg_inf) continue;
+#endif
             if (a.s ^ b.s) neg_inf = 1; else pos_inf = 1;
         }
     }
@@ -836,7 +844,9 @@ static uint32_t acc_bits_with_c(const operands *o, int64_t m, int64_t n, uint32_
     int cls = special_class(o, m, n, &neg);
     if (ce == 0xFFu) {
         if (cls == CLS_NAN) return CANON_NAN_F32;
+#if ORACLE_MUTANT != MUT_C_INF_ABSORBS
         if (cls == CLS_INF && neg != (int)(c_in >> 31)) return CANON_NAN_F32;
+#endif
         return c_in;
     }
     if (cls == CLS_NAN) return CANON_NAN_F32;

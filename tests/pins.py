@@ -507,7 +507,92 @@ def pin_c_composition(o, trials=12, seed=37):
         assert (zero == whole).all(), (t, "c = +0", _first_diff(zero, whole))
 
 
+def _ieee_class(v: float) -> int:
+    """The binary32 accumulator a non-finite float64 value stands for (NaN
+    canonical), or None for a finite one."""
+    if math.isnan(v):
+        return CANON32
+    if math.isinf(v):
+        return 0x7F800000 if v > 0 else 0xFF800000
+    return None
+
+
+def _rows_with_infinities(rng, gen, rows, K, fmt):
+    """Finite e5m2 rows, a third of them with one to four infinities of random
+    signs, a few with +Inf only or -Inf only."""
+    r = _random_finite(rng, gen, (rows, K), fmt)
+    for i in range(rows):
+        kind = i % 3
+        if kind == 0:
+            continue
+        ks = rng.choice(K, int(rng.integers(1, 5)), replace=False)
+        signs = rng.integers(0, 2, len(ks)) if kind == 1 else np.full(len(ks), i % 2)
+        r[i, ks] = (0x7C | (signs << 7)).astype(np.uint8)
+    return r
+
+
+def pin_infinities_ieee(o, trials=24, seed=41):
+    """E5M2 infinities (the reading: the IEEE outcome of the products' sum):
+    the oracle's accumulator is NaN, +Inf or -Inf exactly where float64 IEEE
+    arithmetic on the torch-decoded values gives that (Inf times a zero is
+    NaN, infinite products of both signs add to NaN), for every split count,
+    both accumulation modes and both profiles (the outcome of a row does not
+    depend on how its products are grouped), and finite elsewhere.  The
+    partner operand gets zeros at some of the infinities' positions."""
+    rng = np.random.default_rng(seed)
+    with np.errstate(invalid="ignore"):
+        for t in range(trials):
+            e5_is_x = t % 2 == 0
+            K = int(rng.choice([16, 48, 96, 160]))
+            gen = torch.Generator().manual_seed(seed + t)
+            e5 = _rows_with_infinities(rng, gen, 6, K, "e5m2")
+            ot = _random_finite(rng, gen, (5, K), "e4m3fn")
+            inf_k = np.argwhere((e5 & 0x7F) == 0x7C)
+            for j in range(0, len(inf_k), 3):  # a zero partner for every third infinity
+                ot[int(rng.integers(0, 5)), inf_k[j][1]] = 0x00 if j % 2 else 0x80
+            x, xf, w, wf = (e5, "e5m2", ot, "e4m3fn") if e5_is_x else (ot, "e4m3fn", e5, "e5m2")
+            xv, wv = torch_decode(x, xf), torch_decode(w, wf)
+            want = [[_ieee_class(float(np.sum(xv[m] * wv[n]))) for n in range(w.shape[0])]
+                    for m in range(x.shape[0])]
+            for profile, fast, S in (("hopper", True, 1), ("hopper", False, 1), ("hopper", True, 3),
+                                     ("ada-pairwise", True, 5), ("ada-serial", False, 2)):
+                acc, _ = o.scaled_mm(x, xf, w, wf, 0x3F800000, 0x3F800000, "fp32", fast, S, profile=profile)
+                for m in range(x.shape[0]):
+                    for n in range(w.shape[0]):
+                        got = int(acc[m, n])
+                        if want[m][n] is None:
+                            assert (got & 0x7F800000) != 0x7F800000, (t, profile, fast, S, m, n, hex(got))
+                        else:
+                            assert got == want[m][n], (t, profile, fast, S, m, n, hex(got), hex(want[m][n]))
+
+
+def pin_c_nonfinite_ieee(o, trials=16, seed=43):
+    """Non-finite incoming accumulators (the reading: IEEE addition of c and
+    the products' sum): with c_in NaN, +Inf or -Inf, and products with and
+    without infinities, the oracle's accumulator is what float64 IEEE
+    arithmetic gives for c + sum(products) whenever that is non-finite."""
+    rng = np.random.default_rng(seed)
+    cs = np.array([0x7FC00000, 0xFFFFFFFF, 0x7F800000, 0xFF800000], dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        for t in range(trials):
+            profile = "hopper" if t % 2 == 0 else "ada-serial"
+            K = int(rng.choice([16, 64, 96]))
+            gen = torch.Generator().manual_seed(seed + t)
+            x = _random_finite(rng, gen, (4, K), "e4m3fn")
+            w = _rows_with_infinities(rng, gen, 6, K, "e5m2")
+            c = cs[rng.integers(0, len(cs), (4, 6))]
+            acc = o.accumulate_c(x, "e4m3fn", w, "e5m2", c, profile=profile)
+            xv, wv = torch_decode(x, "e4m3fn"), torch_decode(w, "e5m2")
+            cv = f32(c).astype(np.float64)
+            for m in range(4):
+                for n in range(6):
+                    want = _ieee_class(float(cv[m, n] + np.sum(xv[m] * wv[n])))
+                    assert want is not None
+                    assert int(acc[m, n]) == want, (t, profile, m, n, hex(int(c[m, n])), hex(int(acc[m, n])),
+                                                    hex(want))
+
+
 # The quick suite the mutation tests run on every mutant.
 QUICK = [pin_golden, pin_code_pairs, pin_zero_rules, pin_sign_symmetry,
          pin_no_truncation_bruteforce, pin_power_of_two_scaling, pin_block_permutation,
-         pin_split_invariants, pin_c_only, pin_c_composition]
+         pin_split_invariants, pin_c_only, pin_c_composition, pin_infinities_ieee, pin_c_nonfinite_ieee]

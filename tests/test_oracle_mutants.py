@@ -34,6 +34,9 @@ MUTANTS = {
     21: "scale_result folded into alpha",
     22: "FP8 outputs overflow instead of saturating",
     23: "subnormal incoming accumulator aligned at its own exponent",
+    24: "an infinity times a zero taken as the infinity",
+    25: "infinite products of both signs taken as the first one's infinity",
+    26: "an infinite incoming accumulator absorbing the opposite infinity",
 }
 
 

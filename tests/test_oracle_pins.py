@@ -65,3 +65,11 @@ def test_accumulator_only_path(o):
 
 def test_incoming_accumulator_composes_chains(o):
     pins.pin_c_composition(o)
+
+
+def test_infinities_follow_ieee(o):
+    pins.pin_infinities_ieee(o)
+
+
+def test_nonfinite_incoming_accumulators_follow_ieee(o):
+    pins.pin_c_nonfinite_ieee(o)
