@@ -405,13 +405,15 @@ def test_deferred_infinities_slow_grid(dev, orc, MN, S, profile):
         api.force_defer(prev)
 
 
-def test_deferred_infinities_workload(dev, orc):
+@pytest.mark.parametrize("profile,S", [("hopper", 1), ("ada-pairwise", 3)])
+def test_deferred_infinities_workload(dev, orc, profile, S):
     """The 8192^3 e4m3fn x e5m2 workload with one w code in 1,000 an
     infinity (random signs), some w rows with 64, 65 or K infinities and a
     few NaN rows in both operands: the automatic plan defers the infinities
     (2^39 multiply-adds); every output must equal the main kernel's own
     handling (deferral forced off), and sampled outputs, a third of them in
-    NaN or infinity rows, the oracle's."""
+    NaN or infinity rows, the oracle's.  Also with the ada profile in three
+    splits (the fix-up after the pairwise combination)."""
     wl = WORKLOADS["mixed_8192"]
     x, w = make_operands(wl, 0)
     gen = torch.Generator().manual_seed(2000)
@@ -423,13 +425,15 @@ def test_deferred_infinities_workload(dev, orc):
     _listed_infinities(w[200:213], rng)
     w[300, 4000] = 0x7E                                              # e5m2 NaN
     x[400, 17] = 0xFF                                                # e4m3fn NaN
-    assert api.workspace_bytes(wl.M, wl.N, wl.K, 1, True) == wl.N * 65 * 4
-    note("[gpu] mixed_8192 with infinities: deferred (automatic)")
-    y, acc = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S)
+    part = S * wl.M * wl.N * 4 if S > 1 else 0
+    assert api.workspace_bytes(wl.M, wl.N, wl.K, S, True, profile) == part + wl.N * 65 * 4
+    note(f"[gpu] mixed_8192 with infinities {profile} S={S}: deferred (automatic)")
+    y, acc = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, S, profile=profile)
     prev = api.force_defer("off")
     try:
-        note("[gpu] mixed_8192 with infinities: in the main kernel")
-        y0, acc0 = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, wl.split_S)
+        note(f"[gpu] mixed_8192 with infinities {profile} S={S}: in the main kernel")
+        y0, acc0 = gpu_run(dev, x, wl.xfmt, w, wl.wfmt, wl.scale_x, wl.scale_w, wl.out, wl.fast, S,
+                           profile=profile)
     finally:
         api.force_defer(prev)
     assert_same(acc, acc0, "deferred vs in-kernel infinities, accumulator")
@@ -439,7 +443,7 @@ def test_deferred_infinities_workload(dev, orc):
         [100] * 10 + [300] * 10 + list(range(200, 213)) * 3 + [209]
     ms, ns = np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
     acc_o, y_o = orc.points(x.numpy(), wl.xfmt, w.numpy(), wl.wfmt, ms, ns, scale_bits(wl.scale_x),
-                            scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S)
+                            scale_bits(wl.scale_w), wl.out, wl.fast, S, profile=profile)
     assert_same(acc[ms, ns], acc_o, "mixed_8192 with infinities, accumulator")
     assert_same(y[ms, ns], y_o, "mixed_8192 with infinities, output")
     nonfinite = int(((acc_o & 0x7F800000) == 0x7F800000).sum())
