@@ -251,6 +251,14 @@ int choose_tile(int64_t M, int64_t N, int S)
             best = c.cfg;
         }
     }
+    // The 32x32 tile staging 4 K-blocks per barrier instead of 2 hides more
+    // load latency, but its 78 KB of LDS leave room for two workgroups per
+    // CU; measured on MI355X it wins while the grid fits in that (64 x 5760 x
+    // 1920, 360 workgroups: 0.167 against 0.173 ms; 256 x 2048 x 4096, 512:
+    // 0.349 against 0.364 ms) and loses beyond (128 x 5760 x 1920, 720:
+    // 0.257 against 0.234 ms).
+    if (best == emu::TILE_32x32 && ((M + 31) / 32) * ((N + 31) / 32) * (int64_t)S <= 2 * 256)
+        best = emu::TILE_32x32_S4;
     return best;
 }
 

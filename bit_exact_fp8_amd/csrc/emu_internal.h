@@ -110,7 +110,9 @@ struct CombineParams {
 // Tile configurations of the main kernel: rows x cols per workgroup; per
 // thread 4x8, 4x4, 2x4, 2x2 outputs, or one output chain shared by 2 or 4
 // lanes (G2, G4; these stage 8 K-blocks per barrier); MX: block exponent
-// maxima on the matrix cores (16x64: one wave, for few rows).
+// maxima on the matrix cores (16x64: one wave, for few rows).  The 32x32
+// tile stages 2 K-blocks per barrier, and 4 in its S4 form (78 KB of LDS:
+// two workgroups per CU, for grids that leave the GPU at most that full).
 enum TileConfig : int {
     TILE_64x128 = 0,
     TILE_64x64 = 1,
@@ -122,7 +124,8 @@ enum TileConfig : int {
     TILE_64x128_MX = 7,
     TILE_16x8_G4 = 8,
     TILE_16x64_MX = 9,
-    TILE_COUNT = 10
+    TILE_32x32_S4 = 10,
+    TILE_COUNT = 11
 };
 
 struct TileShape {

@@ -1333,13 +1333,14 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_64x128: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, false, BLK>(p, S, stream);
     case TILE_64x64: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, false, BLK>(p, S, stream);
     case TILE_32x64: return launch_cfg<XF, WF, 32, 64, 2, 4, 1, false, BLK>(p, S, stream);
-    case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK>(p, S, stream);
+    case TILE_32x32: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 2>(p, S, stream);
     case TILE_16x16_G2: return launch_cfg<XF, WF, 16, 16, 1, 1, 2, false, BLK, 8>(p, S, stream);
     case TILE_16x16_G4: return launch_cfg<XF, WF, 16, 16, 1, 1, 4, false, BLK, 8>(p, S, stream);
     case TILE_64x64_MX: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_64x128_MX: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, S, stream);
     case TILE_16x8_G4: return launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, S, stream);
     case TILE_16x64_MX: return launch_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, S, stream);
+    case TILE_32x32_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1372,13 +1373,14 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream)
     case TILE_64x128: return launch_cin_cfg<XF, WF, 64, 128, 4, 8, 1, false, BLK>(p, stream);
     case TILE_64x64: return launch_cin_cfg<XF, WF, 64, 64, 4, 4, 1, false, BLK>(p, stream);
     case TILE_32x64: return launch_cin_cfg<XF, WF, 32, 64, 2, 4, 1, false, BLK>(p, stream);
-    case TILE_32x32: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK>(p, stream);
+    case TILE_32x32: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 2>(p, stream);
     case TILE_16x16_G2: return launch_cin_cfg<XF, WF, 16, 16, 1, 1, 2, false, BLK, 8>(p, stream);
     case TILE_16x16_G4: return launch_cin_cfg<XF, WF, 16, 16, 1, 1, 4, false, BLK, 8>(p, stream);
     case TILE_64x64_MX: return launch_cin_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_64x128_MX: return launch_cin_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, stream);
     case TILE_16x8_G4: return launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, stream);
     case TILE_16x64_MX: return launch_cin_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, stream);
+    case TILE_32x32_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

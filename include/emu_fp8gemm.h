@@ -212,10 +212,11 @@ EMU_API int emu_abi_version(void);
 /*
  * Testing and tuning: force the main kernel's tile configuration for every
  * later call in the process (cfg = -1 restores the automatic choice; valid
- * configurations are 0 .. 9: 64x128, 64x64, 32x64, 32x32 output tiles with
+ * configurations are 0 .. 10: 64x128, 64x64, 32x64, 32x32 output tiles with
  * one lane per output, 16x16 with 2 or 4 lanes per output, 64x64 and
  * 64x128 with the block exponent maxima on the matrix cores, 16x8 with 4
- * lanes per output, 16x64 with matrix-core maxima in one wave).  Results do not
+ * lanes per output, 16x64 with matrix-core maxima in one wave, 32x32
+ * staging 4 K-blocks per barrier).  Results do not
  * depend on the configuration.  Returns the previous setting, or -2 (and
  * changes nothing) for an invalid cfg.  Process-wide; not for concurrent use
  * with calls that expect the automatic choice.
