@@ -65,7 +65,11 @@ constexpr int KB = 32;           // k per LDS stage (one 32-product block or two
 constexpr int KP = KB / 2;       // packed pairs per stage
 constexpr int CHUNK = 128;       // slow-accumulation restart
 constexpr int A_STRIDE = KB + 4; // floats per LDS row of the value plane (16 B pad)
-constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent / sign planes
+constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent planes
+// Words per LDS row of the sign planes: an odd number of 8-byte pairs, so that
+// 16 lanes reading 8 bytes from 16 consecutive rows (the 64x64 and 64x128
+// tiles' w side) use all 32 banks once; rows are 8-byte aligned.
+constexpr int S_STRIDE = KP + 2;
 
 // Exponent planes (one u16 per code).  A nonzero code stores
 // ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
@@ -107,6 +111,11 @@ constexpr uint32_t X_POW_OFF = 5;
 constexpr uint32_t W_POW_OFF = 4;
 constexpr uint32_t POW_TO_EB = 93;
 constexpr int PW_ROW = 8;  // words per (quarter, row) of a power plane: 8 real + 8 zero bf16
+// The four 8-byte chunks of a power-plane row are stored XOR-swizzled by bits
+// 2-3 of the row: a matrix instruction's 16 lanes read one chunk of 16
+// consecutive rows, which unswizzled would fall on 4 bank pairs (rows 8 words
+// apart) and swizzled cover all 32 banks.
+__device__ __forceinline__ int pw_chunk(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
@@ -355,7 +364,8 @@ __device__ __forceinline__ uint32_t power_pair(uint32_t p)
 // Decode 16 consecutive codes of one row into the value and sign planes and
 // the power plane (the two quarter-blocks the 16 codes cover, 8 codes each).
 template <int FMT, uint32_t OFF>
-__device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *vs, uint32_t *pq0, uint32_t *pq1)
+__device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *vs, uint32_t *pq0, uint32_t *pq1,
+                                                int row)
 {
     const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[16];
@@ -374,10 +384,12 @@ __device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *
     for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-        *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
-    *reinterpret_cast<uint4 *>(pq0) = make_uint4(pp[0], pp[1], pp[2], pp[3]);
-    *reinterpret_cast<uint4 *>(pq1) = make_uint4(pp[4], pp[5], pp[6], pp[7]);
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2 *>(vs + 2 * q) = make_uint2(sp[2 * q], sp[2 * q + 1]);
+    // the quarter's 8 codes are chunks 0 and 1 of its row (chunks 2 and 3 stay zero)
+    *reinterpret_cast<uint2 *>(pq0 + 2 * pw_chunk(row, 0)) = make_uint2(pp[0], pp[1]);
+    *reinterpret_cast<uint2 *>(pq0 + 2 * pw_chunk(row, 1)) = make_uint2(pp[2], pp[3]);
+    *reinterpret_cast<uint2 *>(pq1 + 2 * pw_chunk(row, 0)) = make_uint2(pp[4], pp[5]);
+    *reinterpret_cast<uint2 *>(pq1 + 2 * pw_chunk(row, 1)) = make_uint2(pp[6], pp[7]);
 }
 
 // Decode 16 consecutive codes of one row into the LDS planes.
@@ -404,10 +416,10 @@ __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve,
     for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q)
         *reinterpret_cast<uint4 *>(ve + 4 * q) = make_uint4(ep[4 * q], ep[4 * q + 1], ep[4 * q + 2], ep[4 * q + 3]);
-        *reinterpret_cast<uint4 *>(vs + 4 * q) = make_uint4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
-    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2 *>(vs + 2 * q) = make_uint2(sp[2 * q], sp[2 * q + 1]);
 }
 
 // Any NaN (E4M3FN) or Inf / NaN (E5M2) code among four packed codes: the
@@ -636,14 +648,15 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr bool RANGED = CHUNKS || SPEC;  // a group of 128-chunks of the split's k-list per workgroup
     static_assert(!SPEC || MX, "speculated exponents use the matrix-core maximum");
     constexpr int XA = BM * A_STRIDE, XP = BM * P_STRIDE, WA = BN * A_STRIDE, WP = BN * P_STRIDE;
+    constexpr int XS = BM * S_STRIDE, WS = BN * S_STRIDE;
 
     // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
     __shared__ __attribute__((aligned(16))) float xa_all[SS * XA];
     __shared__ __attribute__((aligned(16))) uint32_t xe_all[MX ? 4 : SS * XP];
-    __shared__ __attribute__((aligned(16))) uint32_t xs_all[SS * XP];
+    __shared__ __attribute__((aligned(16))) uint32_t xs_all[SS * XS];
     __shared__ __attribute__((aligned(16))) float wa_all[SS * WA];
     __shared__ __attribute__((aligned(16))) uint32_t we_all[MX ? 4 : SS * WP];
-    __shared__ __attribute__((aligned(16))) uint32_t wsg_all[SS * WP];
+    __shared__ __attribute__((aligned(16))) uint32_t wsg_all[SS * WS];
     __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
     __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
     __shared__ uint32_t flags[BM + BN + CHUNKS];  // per row (and, for stored chunks, their union)
@@ -783,30 +796,30 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         has_special<XF>(raw[q].w))
                         myflag[q] |= special_flags<XF>(raw[q]);  // rare: NaN / Inf codes
                     float *xa = xa_all + st * XA;
-                    uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XP;
+                    uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XS;
                     if (MX)
                         decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                       xs + r * P_STRIDE + 8 * half,
+                                                       xs + r * S_STRIDE + 8 * half,
                                                        xp + ((2 * half) * BM + r) * PW_ROW,
-                                                       xp + ((2 * half + 1) * BM + r) * PW_ROW);
+                                                       xp + ((2 * half + 1) * BM + r) * PW_ROW, r);
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                  xe + r * P_STRIDE + 8 * half, xs + r * P_STRIDE + 8 * half);
+                                                  xe + r * P_STRIDE + 8 * half, xs + r * S_STRIDE + 8 * half);
                 } else {
                     const int rw = r - BM;
                     if (has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) | has_special<WF>(raw[q].z) |
                         has_special<WF>(raw[q].w))
                         myflag[q] |= special_flags<WF>(raw[q]);  // rare: NaN / Inf codes
                     float *wa = wa_all + st * WA;
-                    uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WP;
+                    uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WS;
                     if (MX)
                         decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
-                                                       wsg + rw * P_STRIDE + 8 * half,
+                                                       wsg + rw * S_STRIDE + 8 * half,
                                                        wp + ((2 * half) * BN + rw) * PW_ROW,
-                                                       wp + ((2 * half + 1) * BN + rw) * PW_ROW);
+                                                       wp + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
-                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * P_STRIDE + 8 * half);
+                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * S_STRIDE + 8 * half);
                 }
             }
         }
@@ -820,7 +833,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         if (spos >= pos_end) break;  // uniform across the workgroup
         const float *xa = xa_all + st * XA, *wa = wa_all + st * WA;
         const uint32_t *xe = xe_all + (MX ? 0 : st * XP), *we = we_all + (MX ? 0 : st * WP);
-        const uint32_t *xs = xs_all + st * XP, *wsg = wsg_all + st * WP;
+        const uint32_t *xs = xs_all + st * XS, *wsg = wsg_all + st * WS;
 #pragma unroll
         for (int hb = 0; hb < NBS; ++hb) {
             uint32_t Cb[RM][RN];
@@ -833,11 +846,11 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 for (int qq = 0; qq < QPB; ++qq) {
                     const int qb = hb * QPB + qq;
                     const s4 a = *reinterpret_cast<const s4 *>(xp + (qb * BM + 16 * wave + (lane & 15)) * PW_ROW +
-                                                               2 * (lane >> 4));
+                                                               2 * pw_chunk(lane & 15, lane >> 4));
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
                         const s4 b = *reinterpret_cast<const s4 *>(wp + (qb * BN + 16 * j + (lane & 15)) * PW_ROW +
-                                                                   2 * (lane >> 4));
+                                                                   2 * pw_chunk(lane & 15, lane >> 4));
                         const f4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
@@ -953,12 +966,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
                 for (int i = 0; i < RM; ++i) {
                     av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
-                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * P_STRIDE + 2 * k4);
+                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * S_STRIDE + 2 * k4);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
-                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * P_STRIDE + 2 * k4);
+                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * S_STRIDE + 2 * k4);
                 }
 #pragma unroll
                 for (int i = 0; i < RM; ++i)
