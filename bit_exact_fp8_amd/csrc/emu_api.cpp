@@ -236,7 +236,7 @@ int choose_tile(int64_t M, int64_t N, int S)
         int cfg;
         double eff;
     };
-    const Cand cands[] = {{emu::TILE_64x64_MX, 1.08}, {emu::TILE_64x128_MX, 0.98}, {emu::TILE_64x64, 0.90},
+    const Cand cands[] = {{emu::TILE_64x64_MX, 1.16}, {emu::TILE_64x128_MX, 1.07}, {emu::TILE_64x64, 0.90},
                           {emu::TILE_64x128, 0.87}, {emu::TILE_32x64, 0.60}, {emu::TILE_32x32, 0.60},
                           {emu::TILE_16x16_G2, 0.30}, {emu::TILE_16x16_G4, 0.24}, {emu::TILE_16x8_G4, 0.24}};
     int best = emu::TILE_16x8_G4;

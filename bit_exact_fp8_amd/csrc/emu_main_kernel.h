@@ -243,25 +243,14 @@ __device__ __forceinline__ uint32_t fma_abs_rz(float a, float b, uint32_t c, uin
 
 // The incoming accumulator's term of a block sum, in units of the block's
 // quantum: |c| cut toward zero by the RTZ fma against C (the low 16 bits of
-// the result, below 2^15), times c's sign.
-// Two forms.  c_block_term_dot: the sign as the 16-bit pair (+-1, 0) and a
-// dot product with the fma result.  c_block_term_med3: the sign from c's
-// bits read as a signed integer, clamped to [-1, 1] (-0 gives -1, which
-// only multiplies a zero magnitude), and a signed 16-bit multiply; one
-// instruction fewer, in one statement so that no wait is placed between its
-// three dependent instructions.  Measured on MI355X the second is faster in
-// the 16-product-block kernels and the incoming-accumulator ones (8192^3
-// ada 45.8 against 48.0 ms) and slower in the other 32-product-block ones
-// (8192^3 hopper 45.2 against 44.9 ms), so each kernel takes the faster.
-__device__ __forceinline__ int c_block_term_dot(uint32_t c, uint32_t Cb, uint32_t tok)
-{
-    const uint32_t rc = fma_abs_rz(__uint_as_float(c), 1.0f, Cb, tok);
-    const uint32_t sc = ((uint32_t)((int)c >> 31) & 0xFFFFu) | 1u;
-    int r;
-    asm("v_dot2_i32_i16 %0, %1, %2, 0" : "=v"(r) : "v"(rc), "v"(sc));
-    return r;
-}
-__device__ __forceinline__ int c_block_term_med3(uint32_t c, uint32_t Cb, uint32_t tok)
+// the result, below 2^15), times c's sign: the sign from c's bits read as a
+// signed integer, clamped to [-1, 1] (-0 gives -1, which only multiplies a
+// zero magnitude), and a signed 16-bit multiply, in one statement so that no
+// wait is placed between its three dependent instructions.  (A form with the
+// sign as the 16-bit pair (+-1, 0) and a dot product takes one instruction
+// more; on MI355X it measured slower in every kernel once the LDS planes were
+// free of bank conflicts: 8192^3 hopper 43.4 against 42.3 ms.)
+__device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t tok)
 {
     int acc;
     uint32_t sgn, r;
@@ -740,7 +729,6 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     // Incoming accumulators keep c cut after every block (they select c
     // itself on some blocks), and so does speculation.
     constexpr bool CUT_EACH_BLOCK = CIN || SPEC;
-    constexpr bool C_TERM_MED3 = BLK == 16 || CIN;  // see c_block_term_dot
     uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -877,8 +865,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                             // the hopper incoming-accumulator kernel: left out there)
                             if constexpr (!(CIN && BLK == 32)) asm("" : "+v"(cb));
                             Cb[i][j] = cb;
-                            acc[i][j] = C_TERM_MED3 ? c_block_term_med3(c[i][j], Cb[i][j], tok)
-                                                    : c_block_term_dot(c[i][j], Cb[i][j], tok);
+                            acc[i][j] = c_block_term(c[i][j], Cb[i][j], tok);
                             if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                         }
                     }
@@ -949,8 +936,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         uint32_t cb = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
                         asm("" : "+v"(cb));  // later uses derive from C itself
                         Cb[i][j] = cb;
-                        const int ct = C_TERM_MED3 ? c_block_term_med3(c[i][j], Cb[i][j], tok)
-                                                   : c_block_term_dot(c[i][j], Cb[i][j], tok);
+                        const int ct = c_block_term(c[i][j], Cb[i][j], tok);
                         acc[i][j] = (G == 1 || lane_g == 0) ? ct : 0;  // c enters the block sum once
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
