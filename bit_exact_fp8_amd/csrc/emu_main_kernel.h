@@ -68,8 +68,14 @@ constexpr int A_STRIDE = KB + 4; // floats per LDS row of the value plane (16 B 
 constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent planes
 // Words per LDS row of the sign planes: an odd number of 8-byte pairs, so that
 // 16 lanes reading 8 bytes from 16 consecutive rows (the 64x64 and 64x128
-// tiles' w side) use all 32 banks once; rows are 8-byte aligned.
-constexpr int S_STRIDE = KP + 2;
+// tiles' w side) use all 32 banks once; rows are 8-byte aligned.  Tiles whose
+// G lanes share an output read G slices of few rows, which no stride spreads
+// over all banks; measured on MI355X (16 x 256 x 65536, 8 splits, A/B in one
+// session) 16-product blocks run faster with the exponent planes' stride
+// (0.151 against 0.155 ms) and 32-product blocks with this one (0.130 against
+// 0.132 ms).
+template <int G, int BLK>
+constexpr int sign_stride() { return (G == 1 || BLK == 32) ? KP + 2 : P_STRIDE; }
 
 // Exponent planes (one u16 per code).  A nonzero code stores
 // ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
@@ -571,10 +577,14 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // Workgroup tile BM x BN outputs of one split; thread tile RM x RN with rows
 // tm + i*TM and columns tn + j*TN (interleaved, so that the lanes of a wave
 // read consecutive, padded LDS rows).
-// Minimum waves per SIMD the register allocation must allow for a thread tile.
-template <int RM, int RN>
+// Minimum waves per SIMD the register allocation must allow for a thread tile
+// (SPEC: the exponent-speculation kernel, which spills at 3 waves with 4x4).
+// Without the bound of 3 for 4x4 tiles the compiler gave the 64x64
+// matrix-core kernel of incoming accumulators 200 VGPRs (2 waves per SIMD),
+// which cost it 3% on 8192^3 (49.3 against 47.7 ms).
+template <int RM, int RN, bool SPEC>
 struct WavesPerSimd {
-    static constexpr int value = (RM * RN >= 16) ? 2 : 4;
+    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16) ? (SPEC ? 2 : 3) : 4;
 };
 
 // G lanes share each output chain (G = 1, 2 or 4): lane g of a chain takes
@@ -614,7 +624,7 @@ constexpr uint32_t SPEC_PRODUCTS_REACH_E = 1u << 29;
 constexpr uint32_t SPEC_SPECIAL = 1u << 31;
 
 template <int XF, int WF, int BM, int BN, int RM, int RN, int G, int ACC, bool MX, int BLK, int SS>
-__global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
+__global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN, ACC == ACC_SPEC>::value)) void main_kernel(MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
     static_assert(BLK == 32 || BLK == 16, "blocks of 32 or 16 products");
@@ -637,7 +647,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr bool RANGED = CHUNKS || SPEC;  // a group of 128-chunks of the split's k-list per workgroup
     static_assert(!SPEC || MX, "speculated exponents use the matrix-core maximum");
     constexpr int XA = BM * A_STRIDE, XP = BM * P_STRIDE, WA = BN * A_STRIDE, WP = BN * P_STRIDE;
-    constexpr int XS = BM * S_STRIDE, WS = BN * S_STRIDE;
+    constexpr int SST = sign_stride<G, BLK>();
+    constexpr int XS = BM * SST, WS = BN * SST;
 
     // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
     __shared__ __attribute__((aligned(16))) float xa_all[SS * XA];
@@ -787,12 +798,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XS;
                     if (MX)
                         decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                       xs + r * S_STRIDE + 8 * half,
+                                                       xs + r * SST + 8 * half,
                                                        xp + ((2 * half) * BM + r) * PW_ROW,
                                                        xp + ((2 * half + 1) * BM + r) * PW_ROW, r);
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                  xe + r * P_STRIDE + 8 * half, xs + r * S_STRIDE + 8 * half);
+                                                  xe + r * P_STRIDE + 8 * half, xs + r * SST + 8 * half);
                 } else {
                     const int rw = r - BM;
                     if (has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) | has_special<WF>(raw[q].z) |
@@ -802,12 +813,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WS;
                     if (MX)
                         decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
-                                                       wsg + rw * S_STRIDE + 8 * half,
+                                                       wsg + rw * SST + 8 * half,
                                                        wp + ((2 * half) * BN + rw) * PW_ROW,
                                                        wp + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
-                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * S_STRIDE + 8 * half);
+                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * SST + 8 * half);
                 }
             }
         }
@@ -952,12 +963,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
                 for (int i = 0; i < RM; ++i) {
                     av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
-                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * S_STRIDE + 2 * k4);
+                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * SST + 2 * k4);
                 }
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
-                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * S_STRIDE + 2 * k4);
+                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * SST + 2 * k4);
                 }
 #pragma unroll
                 for (int i = 0; i < RM; ++i)
