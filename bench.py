@@ -104,6 +104,64 @@ def cpu_baseline(wl, x, w, y_gpu, budget_s: float, profile: str = "hopper"):
             "gpu_bit_exact_on_sample": same}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rates():
+    """The CPU oracle's own rates on the host, no GPU involved: the C oracle
+    on one thread over the tiny workload and a row sample of the projection,
+    the same on all threads (up to 16) over the projection, and the exact
+    Python (Fraction) specification on one thread over the tiny workload,
+    checked bit for bit against the C oracle there."""
+    import oracle
+    from oracle import spec
+    orc = oracle.default()
+    threads = min(16, os.cpu_count() or 1)
+    res = {"cpu": cpu_model(), "host_threads": os.cpu_count(), "threads_used": threads}
+
+    def timed(fn, min_s=1.0):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            out = fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                return out, dt / reps
+
+    for name, rows, nthreads, key in (("tiny", None, 1, "c_oracle_1thread_tiny"),
+                                      ("proj_64x5760x1920", 16, 1, "c_oracle_1thread_proj"),
+                                      ("proj_64x5760x1920", None, threads, "c_oracle_all_threads_proj")):
+        wl = WORKLOADS[name]
+        x, w = make_operands(wl, 0)
+        xs = x.numpy() if rows is None else x.numpy()[:rows]
+        m = xs.shape[0]
+        _, dt = timed(lambda: orc.scaled_mm(xs, wl.xfmt, w.numpy(), wl.wfmt, scale_bits(wl.scale_x),
+                                            scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S, threads=nthreads))
+        res[key] = {"gemm_ops_per_s": 2 * m * wl.N * wl.K / dt, "threads": nthreads,
+                    "sample": f"{m} x {wl.N} x {wl.K}", "seconds": dt}
+    wl = WORKLOADS["tiny"]
+    x, w = make_operands(wl, 0)
+    t0 = time.perf_counter()
+    _, ys = spec.scaled_mm(x.numpy().tolist(), wl.xfmt, w.numpy().tolist(), wl.wfmt, scale_bits(wl.scale_x),
+                           scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S)
+    dt = time.perf_counter() - t0
+    _, yc = orc.scaled_mm(x.numpy(), wl.xfmt, w.numpy(), wl.wfmt, scale_bits(wl.scale_x),
+                          scale_bits(wl.scale_w), wl.out, wl.fast, wl.split_S, threads=1)
+    res["python_spec_1thread_tiny"] = {"gemm_ops_per_s": 2 * wl.M * wl.N * wl.K / dt, "threads": 1,
+                                       "sample": f"{wl.M} x {wl.N} x {wl.K}", "seconds": dt,
+                                       "equals_c_oracle": bool(np.array_equal(np.array(ys, dtype=np.uint32),
+                                                                              yc.astype(np.uint32)))}
+    print(json.dumps({"oracle_rates": res}), flush=True)
+
+
 def copy_reference(mib: int):
     """A plain device-to-device copy of a known size: reads and writes
     mib MiB once each.  Profiling it gives the scale of the HBM byte
@@ -169,7 +227,13 @@ def main():
                     help="time emu_accumulate_c (chains from incoming accumulators) instead of emu_scaled_mm")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--oracle-rates", action="store_true",
+                    help="only time the CPU oracle (C on 1 and all threads, Python spec on 1) on the host")
     args = ap.parse_args()
+
+    if args.oracle_rates:
+        oracle_rates()
+        return
 
     if args.copy_reference:
         copy_reference(args.copy_reference)
@@ -286,6 +350,7 @@ def main():
             "traffic": traffic,
             "launch_ms": launch_ms,
             "launch_ms_min": float(np.min(ev_ms)),
+            "launch_ms_median": float(np.median(ev_ms)),
         },
     }
     if not args.no_cpu_baseline:
