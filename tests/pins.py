@@ -596,3 +596,58 @@ def pin_c_nonfinite_ieee(o, trials=16, seed=43):
 QUICK = [pin_golden, pin_code_pairs, pin_zero_rules, pin_sign_symmetry,
          pin_no_truncation_bruteforce, pin_power_of_two_scaling, pin_block_permutation,
          pin_split_invariants, pin_c_only, pin_c_composition, pin_infinities_ieee, pin_c_nonfinite_ieee]
+
+
+# ---------------------------------------------------------------------------
+# Per-profile cross-check: 10^4 outputs for each profile and accumulation mode
+def _spec_batch(job):
+    """The Fraction formulation over one batch (a process-pool task)."""
+    x, xf, w, wf, sx, sw, out, fast, S, prof = job
+    return spec.scaled_mm(x, xf, w, wf, sx, sw, out, fast, S, prof["B"], prof["F"], prof["Q"], prof["W"],
+                          prof["layout"], prof["combine"])
+
+
+def spec_profile_jobs(profile: str, fast: bool, seed: int, side=50, Ks=(16, 48, 96, 160)):
+    """Batches of side x side outputs (every pair of side x rows and side w
+    rows) at each K: chains over 1 to 10 blocks, slow-mode restarts at 128
+    (K = 160), several splits, non-power-of-two scales, every output type but
+    FP8, zeros in one batch and NaN / Inf codes in another."""
+    import oracle
+    prof = oracle.PROFILES[profile]
+    rng = np.random.default_rng(seed)
+    pyr = random.Random(seed)
+    jobs = []
+    for b, K in enumerate(Ks):
+        xf, wf = (("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn"), ("e4m3fn", "e5m2"))[b % 4]
+        x = rng.integers(0, 256, (side, K), dtype=np.uint8)
+        w = rng.integers(0, 256, (side, K), dtype=np.uint8)
+        if b != 1:  # batch 1 keeps its random NaN / Inf codes
+            x[(x & 0x7F) >= 0x7C] &= 0x8F
+            w[(w & 0x7F) >= 0x7C] &= 0x8F
+        if b == 2:
+            x[rng.random((side, K)) < 0.3] = 0
+            w[rng.random((side, K)) < 0.3] = 0x80
+        S = (1, 2, 3, 2)[b]
+        sx = int(bits32(np.float32(pyr.choice([1 / 64, 0.1, -3.0, 1 / 3]))))
+        sw = int(bits32(np.float32(pyr.choice([1 / 32, 1 / 3, 7.0, 0.3]))))
+        out = ("bf16", "fp16", "fp32", "bf16")[b]
+        jobs.append((x.tolist(), xf, w.tolist(), wf, sx, sw, out, fast, S, dict(prof)))
+    return jobs
+
+
+def pin_spec_cross_check_profiles(o, seed=47):
+    """The C oracle equals the Fraction formulation on 10^4 outputs for each
+    profile (hopper, ada-serial, ada-pairwise) and each accumulation mode."""
+    from concurrent.futures import ProcessPoolExecutor
+    cases = [(p, fast) for p in ("hopper", "ada-serial", "ada-pairwise") for fast in (True, False)]
+    all_jobs = [(case, job) for i, case in enumerate(cases) for job in spec_profile_jobs(*case, seed + i)]
+    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        want = list(ex.map(_spec_batch, [job for _, job in all_jobs]))
+    counted = {}
+    for ((profile, fast), job), (acc2, y2) in zip(all_jobs, want):
+        x, xf, w, wf, sx, sw, out, _, S, _ = job
+        acc, y = o.scaled_mm(np.array(x, dtype=np.uint8), xf, np.array(w, dtype=np.uint8), wf, sx, sw, out,
+                             fast, S, profile)
+        assert acc.tolist() == acc2 and y.tolist() == y2, (profile, fast, xf, wf, len(x[0]), S, out)
+        counted[(profile, fast)] = counted.get((profile, fast), 0) + acc.size
+    assert all(n >= 10_000 for n in counted.values()), counted

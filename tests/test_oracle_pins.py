@@ -73,3 +73,7 @@ def test_infinities_follow_ieee(o):
 
 def test_nonfinite_incoming_accumulators_follow_ieee(o):
     pins.pin_c_nonfinite_ieee(o)
+
+
+def test_spec_cross_check_per_profile_and_mode(o):
+    pins.pin_spec_cross_check_profiles(o)
