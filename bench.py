@@ -344,6 +344,7 @@ def main():
         "roofline": {
             "bound": "alu",
             "achieved": achieved / 1e12,
+            "achieved_tmac_per_s": achieved / 2e12,
             "peak": PEAK_ALU / 1e12,
             "unit": "T GEMM-ops/s",
             "frac": achieved / PEAK_ALU,
