@@ -206,6 +206,29 @@ def test_every_tile_config(dev, orc, cfg, shape, profile):
         api.force_tile(prev)
 
 
+@pytest.mark.parametrize("shape,forced", [
+    ((64, 8192, 288), -1),   # 2 x 256 = 512 workgroups of the 32x32 tile: its 4-stage form
+    ((96, 5472, 224), -1),   # 3 x 171 = 513 workgroups: its 2-stage form
+    ((96, 5472, 224), 10),   # the 4-stage form forced on that grid
+    ((80, 4000, 400), -1),   # ragged rows, columns and K (4-stage form, 375 workgroups)
+])
+def test_stage_forms_of_the_32x32_tile(dev, orc, shape, forced):
+    """The host's choice between the 32x32 tile's 2- and 4-stage forms (at
+    most 512 workgroups take the 4-stage one) gives the oracle's bits on both
+    sides of the boundary, fast and slow, unsplit and split."""
+    M, N, K = shape
+    gen = torch.Generator().manual_seed(M + N + K)
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.05, 0.05, gen)
+    w = inject(random_codes((N, K), "e4m3fn", gen), "e4m3fn", 0.05, 0.05, gen)
+    prev = api.force_tile(forced)
+    try:
+        for fast, S in ((True, 1), (False, 1)):
+            check(dev, orc, x, "e4m3fn", w, "e4m3fn", 0.1, 1 / 3, "bf16", fast, S,
+                  f"32x32 stage forms {shape} tile {forced}")
+    finally:
+        api.force_tile(prev)
+
+
 # ---- dense specials ---------------------------------------------------------------
 @pytest.mark.parametrize("profile,S,fast", [("hopper", 1, True), ("hopper", 3, True), ("ada-pairwise", 5, True),
                                             ("hopper", 1, False), ("ada-serial", 2, False)])
