@@ -229,6 +229,41 @@ def test_stage_forms_of_the_32x32_tile(dev, orc, shape, forced):
         api.force_tile(prev)
 
 
+@pytest.mark.parametrize("seed", [101, 102])
+def test_randomized_cases(dev, orc, seed):
+    """200 seeded random problems per seed: ragged shapes (K = 0 included),
+    every format pair, 1 to 9 splits, fast and slow, every profile, every
+    output type (FP8 with scale_result), the automatic or a forced tile
+    configuration, zeros, subnormals and (in a fifth of them) NaN / Inf
+    codes; each compared bit for bit with the oracle."""
+    import random
+    rnd = random.Random(seed)
+    for c in range(200):
+        M = rnd.choice([1, 2, 15, 16, 17, 33, 64, 65, 100, 128, 200])
+        N = 16 * rnd.randint(1, 48)
+        K = 16 * rnd.choice([0, 1, 2, 3, 7, 8, 9, 16, 17, 33, 64, 65, 96])
+        xf, wf = rnd.choice([("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn")])
+        S = rnd.choice([1, 1, 1, 2, 3, 5, 8, 9])
+        fast = rnd.random() < 0.5
+        profile = rnd.choice(["hopper", "hopper", "ada-serial", "ada-pairwise"])
+        outs = ["bf16", "fp16", "fp32", "e4m3fn"] + ([] if (xf, wf) == ("e4m3fn", "e4m3fn") else ["e5m2"])
+        out = rnd.choice(outs)
+        sr = rnd.choice([0.5, 3.0, 1 / 3]) if out in ("e4m3fn", "e5m2") else None
+        tile = rnd.choice([-1, -1, -1] + list(range(len(api.TILE_CONFIGS))))
+        sx = rnd.choice([1 / 64, 0.1, 1 / 3, -2.5, 7.0])
+        sw = rnd.choice([1 / 32, 0.3, 1 / 3, 4.0])
+        gen = torch.Generator().manual_seed(seed * 100000 + c)
+        finite = rnd.random() < 0.8
+        x = inject(random_codes((M, K), xf, gen, finite=finite), xf, 0.05, 0.05, gen)
+        w = inject(random_codes((N, K), wf, gen, finite=finite), wf, 0.05, 0.05, gen)
+        prev = api.force_tile(tile)
+        try:
+            check(dev, orc, x, xf, w, wf, sx, sw, out, fast, S,
+                  f"random case {seed}/{c} tile {tile} finite={finite}", profile=profile, sr=sr)
+        finally:
+            api.force_tile(prev)
+
+
 # ---- dense specials ---------------------------------------------------------------
 @pytest.mark.parametrize("profile,S,fast", [("hopper", 1, True), ("hopper", 3, True), ("ada-pairwise", 5, True),
                                             ("hopper", 1, False), ("ada-serial", 2, False)])
