@@ -577,11 +577,14 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // Workgroup tile BM x BN outputs of one split; thread tile RM x RN with rows
 // tm + i*TM and columns tn + j*TN (interleaved, so that the lanes of a wave
 // read consecutive, padded LDS rows).
-// Minimum waves per SIMD the register allocation must allow for a thread tile
-// (SPEC: the exponent-speculation kernel, which spills at 3 waves with 4x4).
+// Minimum workgroups per CU the register allocation must allow for a thread
+// tile: the launch bound's second argument, which the compiler caps at what
+// the workgroup's LDS lets fit.  With the 256-thread workgroups of the tiles
+// with one lane per output this is the minimum waves per SIMD (3: at most 168
+// VGPRs).  SPEC: the exponent-speculation kernel, which spills at 3 with 4x4.
 // Without the bound of 3 for 4x4 tiles the compiler gave the 64x64
 // matrix-core kernel of incoming accumulators 200 VGPRs (2 waves per SIMD),
-// which cost it 3% on 8192^3 (49.3 against 47.7 ms).
+// which cost it 9% on 8192^3 (49.3 against 44.7 ms, A/B in one session).
 template <int RM, int RN, bool SPEC>
 struct WavesPerSimd {
     static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16) ? (SPEC ? 2 : 3) : 4;
