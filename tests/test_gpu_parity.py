@@ -576,13 +576,13 @@ def gpu_accumulate_c(dev, x, xfmt, w, wfmt, c_bits, profile="hopper"):
     return bits_of(acc)
 
 
-@pytest.mark.parametrize("tile", [-1, 3, 5, 6, 8, 9])
+@pytest.mark.parametrize("tile", [-1] + list(range(len(api.TILE_CONFIGS))))
 @pytest.mark.parametrize("profile", ["hopper", "ada-serial"])
 def test_incoming_accumulators(dev, orc, profile, tile):
     """Fast chains from incoming accumulators (normal, tiny, subnormal,
     signed zero, infinite, NaN and chain-sized c), on ragged shapes, K = 0,
     rows of zero codes (the accumulator-only path), NaN / Inf codes, every
-    format pair and several tile configurations, against the oracle."""
+    format pair and every tile configuration, against the oracle."""
     rng = np.random.default_rng(41 + tile)
     prev = api.force_tile(tile)
     try:
