@@ -16,8 +16,9 @@ __device__ __forceinline__ uint32_t scale_result_bits(const float *sr)
 }
 
 // out[idx] for accumulator acc: alpha = RN32(sx * sw) (limitations page,
-// corrections table: y32 = fma(acc, alpha, +0) computed exactly; validation
-// page, claims table: bf16 / fp16 rounded from the binary32 value, FP8
+// corrections table: y32 is one fused multiply-add of acc and alpha with a
+// +0 addend, rounded once; validation page, claims table: bf16 / fp16
+// rounded from the binary32 value, FP8
 // outputs take scale_result as a separate binary32 multiplication and
 // saturate).  RN32(y32 * 1) = y32, so sr = 1.0 stands for no scale_result.
 __device__ __forceinline__ void store_epilogue(int out_kind, void *out, int64_t idx, uint32_t acc,

@@ -1,8 +1,9 @@
 // fp_round.h -- IEEE 754 roundings in integer arithmetic, for host and device.
 //
 // The epilogue of the emulated GEMM rounds twice (mmaemu limitations page,
-// corrections table: y = fma(acc, alpha, +0) computed exactly; validation
-// page, claims table: bf16/fp16 outputs rounded from the fp32 value).  These
+// corrections table: y is one fused multiply-add of acc and alpha with a +0
+// addend, rounded once; validation page, claims table: bf16/fp16 outputs
+// rounded from the fp32 value).  These
 // routines do those roundings on bit patterns with integer operations only,
 // so the result never depends on the GPU's floating-point mode register
 // (rounding mode, denormal flushing) or on how the compiler treats float

@@ -47,7 +47,7 @@
 #define MUT_C_NOT_IN_MAX       5  /* incoming accumulator left out of the block maximum */
 #define MUT_NORMALISED_EXP     6  /* product exponent floor(log2|p|) instead of the field sum */
 #define MUT_NEG_ZERO_BLOCK     7  /* a block that sums to zero keeps the sign of the terms */
-#define MUT_CHUNK64            8  /* slow accumulation restarts every 64 instead of 128 */
+#define MUT_CHUNK64            8  /* slow chunks of 64 positions instead of 128 */
 #define MUT_REVERSED_COMBINE   9  /* split partials added in reverse order */
 #define MUT_SINGLE_ROUNDING   10  /* bf16/fp16 rounded straight from the exact product */
 #define MUT_MUL_NOT_FMA       11  /* y32 = RN32(acc*alpha) keeping the product's zero sign */
@@ -95,8 +95,8 @@ typedef struct {
  *
  * A finite code decodes to (-1)^s * M * 2^(e-3) with M an integer holding
  * three fraction bits.  For a subnormal code the exponent is the format's
- * emin, not the exponent of the leading bit: the validation page's claims
- * table states that subnormal inputs keep exponent emin.  E5M2 has two
+ * emin, not the exponent of the leading bit (validation page, claims
+ * table, row on subnormal inputs).  E5M2 has two
  * fraction bits; its M is doubled so both formats share the 2^(e-3) scale.
  */
 typedef struct {
@@ -149,10 +149,11 @@ static fp8_val decode_fp8(uint8_t code, int fmt)
  * A product of two finite nonzero inputs is exact: (-1)^s * P * 2^(g-6) with
  * P = Ma*Mb (at most 225) and g = ea + eb, the sum of the field exponents.
  * Reading: the alignment exponent of a product is this field sum, the product
- * is never renormalised (the claims table's "subnormal inputs keep exponent
- * emin" only has content if the exponents come from the fields).  A product
- * with a zero factor is a zero product: it is excluded from the block maximum
- * (validation page, claims table, first row) and contributes nothing.
+ * is never renormalised (the claims table's row on subnormal inputs, which
+ * places them at emin, only has content if the exponents come from the
+ * fields).  A product with a zero factor is a zero product: it takes no part
+ * in the block maximum (validation page, claims table, first row) and
+ * contributes nothing.
  */
 typedef struct {
     int cls;  /* CLS_ZERO or CLS_FINITE (specials are handled separately) */
@@ -218,13 +219,13 @@ static int64_t scale_floor(int64_t m, int sh)
  *     the block gives +0.
  *  2. The quantum is 2^q with q = E - F: every term keeps F fraction bits
  *     relative to 2^E.
- *  3. Each term, and c, is cut to that quantum toward zero in sign-magnitude
- *     form (claims table: "alignment, carry, sign-magnitude truncation").
+ *  3. Each term, and c, is cut to that quantum toward zero, on the
+ *     magnitude with the sign kept apart (claims table, truncation row).
  *  4. The terms are added exactly.  A sum that is exactly zero gives +0
- *     (scope table row "Ada instruction model": a block result that is
- *     exactly zero or truncates to zero is +0).
- *  5. The sum is cut toward zero to 1+F significant bits ("block sums are
- *     truncated to 13 fraction bits"; the carry case).
+ *     (scope table row "Ada instruction model": zero block results, exact
+ *     or after truncation, are positive zero).
+ *  5. The sum is cut toward zero to 1+F significant bits (claims table,
+ *     truncation row: the block sum keeps 13 fraction bits; the carry case).
  */
 static exact_val block_step(exact_val c, const product *p, int n, int F)
 {
@@ -403,9 +404,10 @@ static float exact_to_f32(exact_val v)
 }
 
 /*
- * Slow accumulation (validation page, H100 claims table: "slow accumulation
- * restarts every 128 elements and adds the chunk results in K order"; scope
- * table row "Slow accumulation": per split when split).
+ * Slow accumulation (validation page, H100 claims table, slow-accumulation
+ * row: a new chain starts at every 128th position and the chunk results are
+ * summed first to last; scope table row "Slow accumulation": per split when
+ * split).
  * Reading: the adder is binary32 round-to-nearest-even and the running sum
  * starts at +0; chunks start at the start of the (split) range.
  */
@@ -439,7 +441,7 @@ static float slow_range(const operands *o, int64_t m, int64_t n, const kseq *ks,
  *
  * Split-K on the RTX 4060 profiles (limitations page, corrections table;
  * validation page, scope table row "Split-K" and claims table): 64-wide
- * k-tiles assigned round-robin to the splits, so split s owns tiles s, s+S,
+ * k-tiles are dealt to the splits in turn, so split s owns tiles s, s+S,
  * s+2S, ... in that order, and its chain (and, for slow accumulation, its
  * chunking) runs along that sequence.
  */
@@ -530,8 +532,8 @@ static float finite_accumulator(const operands *o, int64_t m, int64_t n, int fas
 /*
  * Non-finite inputs, decided per output from the whole rows x[m,:], w[n,:]
  * (limitations page, corrections table; validation page claims table on IEEE
- * specials): a NaN code anywhere in row m of x or row n of w makes the
- * output the canonical NaN.
+ * specials): output (m, n) is the canonical NaN as soon as x's row m or w's
+ * row n holds a NaN code, at any k.
  * Reading (E5M2 infinities; the pages record them but state no rule): a k
  * with Inf times zero, or infinite products of both signs, give NaN;
  * otherwise any infinite product gives that signed infinity.  This is the
@@ -564,8 +566,8 @@ static int special_class(const operands *o, int64_t m, int64_t n, int *neg)
 /* ------------------------------------------------------------------------ */
 /* IEEE round-to-nearest-even of an exact value to a binary format with p
  * significand bits and exponent range [emin, emax], subnormals kept
- * (limitations page: flush-to-zero would change subnormal arithmetic and is
- * refused).  The argument must be exact in double, which every caller
+ * (limitations page: flushing subnormals to zero is refused, since it
+ * alters their arithmetic).  The argument must be exact in double, which every caller
  * guarantees (products of two binary32 values, binary32 values).
  * Returns the rounded value (+-inf on overflow), with the sign of v. */
 static double round_to_format(double v, int p, int emin, int emax)
@@ -620,9 +622,10 @@ static float mul_f32(float a, float b)
 }
 
 /*
- * Epilogue, first rounding (limitations page, corrections table: the
- * epilogue is y = fma(acc, alpha, +0) computed exactly; validation page,
- * scope table row "Epilogue": alpha = fp32(scale_a * scale_b)):
+ * Epilogue, first rounding (limitations page, corrections table: one fused
+ * multiply-add of acc and alpha with +0 as the addend, rounded once;
+ * validation page, scope table row "Epilogue": alpha is the binary32 product
+ * of the two scales):
  * y32 = RN32(acc * alpha + (+0)).  An exactly zero product gives +0 (the
  * sum -0 + +0 is +0 under round to nearest); a nonzero product that rounds
  * to zero keeps its sign; overflow gives infinity.
@@ -645,8 +648,8 @@ static float epilogue_f32(float acc, float alpha)
 }
 
 /* Second rounding: RNE of the binary32 value to the output format
- * (validation page: bf16/fp16 outputs are rounded from the fp32 value,
- * double rounding, shown on constructed ties). */
+ * (validation page, claims table, double-rounding row: bf16 and fp16
+ * outputs are rounded from the binary32 result, not from the exact value). */
 static uint32_t encode_output(float y32, int out_dtype)
 {
     if (out_dtype == OUT_FP32) {
@@ -687,9 +690,9 @@ static uint32_t encode_single_rounded(float acc, float alpha, int out_dtype)
 #endif
 
 /*
- * FP8 outputs (validation page, scope table row "Epilogue": fp8 output with
- * scale_result and saturation; claims table: scale_result is a separate fp32
- * multiply before saturation to the format's maximum):
+ * FP8 outputs (validation page, scope table row "Epilogue" and claims table,
+ * FP8-output rows: scale_result enters through its own binary32
+ * multiplication, and the result saturates at the format's largest value):
  *   y' = RN32(y32 * scale_result), a plain IEEE binary32 multiplication;
  *   |y'| is clamped to the format's largest finite value (448 for e4m3fn,
  *   57344 for e5m2), infinities included;

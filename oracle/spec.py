@@ -31,7 +31,7 @@ def decode(code: int, fmt: str):
     """(kind, sign, field_exponent, value) of an FP8 code.
 
     The field exponent of a subnormal is the format's emin = 1 - bias
-    (validation page, claims table: subnormal inputs keep exponent emin)."""
+    (validation page, claims table, row on subnormal inputs)."""
     ebits, mbits, bias, has_inf = FORMATS[fmt]
     sign = (code >> 7) & 1
     ef = (code >> mbits) & ((1 << ebits) - 1)
