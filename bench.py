@@ -6,10 +6,23 @@ the FP8 operands, scales, output and workspace already resident in HBM.
 Prints one JSON line.
 
 Metric: emulated GEMM-ops/s = 2*M*N*K / t, and the fraction of the
-integer-VALU roofline R.  R counts 7 integer operations per multiply-add
-(exponent add, block maximum, alignment distance, significand product,
-shift-truncate, sign, accumulate) at the packed 16-bit VALU rate:
-256 CUs x 64 lanes x 2.4 GHz x 2 ops / 7 = 22.47e12 GEMM-ops/s.
+integer-VALU ceiling.
+
+roofline.peak (bound "alu") is the VALU issue ceiling of the path's term
+loop, from the chip's unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes x
+2.4 GHz = 3.93e13 VALU lane-slots/s, divided by the 2.5 lane-slots every
+multiply-add needs in the term loop (one truncating FMA per product; one
+byte permute, one sign-pair bitop and one 16-bit dot product per pair of
+products), times 2 ops per multiply-add: 31.46e12 GEMM-ops/s.  Everything
+else the kernel issues (decode, block maxima, per-block prologue and
+epilogue, addressing) is counted against it.  roofline.frac_vs_R is the
+achieved rate over the survey's op-count model R, which charges 7 packed
+16-bit integer operations per multiply-add (exponent add, block maximum,
+alignment distance, significand product, shift-truncate, sign, accumulate):
+256 x 64 x 2.4e9 x 2 / 7 x 2 = 22.47e12 GEMM-ops/s; the kernel fuses several
+of those into one instruction, so it can exceed R.  roofline.issue_peak is
+the same term loop priced at its instructions' measured issue rates
+(profiles/issue_ceiling.json, from the microbenchmark), when present.
 
 cpu_baseline: the CPU oracle, untuned, timed on the host on a bounded sample
 of the same workload (whole rows of the output), and checked bit for bit
@@ -35,7 +48,10 @@ from bit_exact_fp8_amd import api  # noqa: E402
 from bit_exact_fp8_amd.inputs import (FP8_DTYPES, OUT_DTYPES, WORKLOADS, make_operands,  # noqa: E402
                                       scale_bits)
 
-PEAK_ALU = 256 * 64 * 2.4e9 * 2 / 7 * 2  # GEMM-ops/s: (packed int ops/s) / (7 ops per MAC) * (2 ops per MAC)
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9     # VALU lane-slots/s: CUs x SIMDs x lanes per clock x clock
+TERM_LOOP_SLOTS_PER_MAC = 2.5              # fma + (perm + bitop3 + dot2c) / 2
+PEAK_ALU = VALU_LANE_SLOTS / TERM_LOOP_SLOTS_PER_MAC * 2   # GEMM-ops/s
+R_MODEL = 256 * 64 * 2.4e9 * 2 / 7 * 2    # the survey's op-count model: 7 packed ops per MAC
 METRIC = "bit-exact emulated FP8 GEMM ops/s (2MNK/s) and % of int-VALU roofline"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -74,11 +90,28 @@ def load_traffic(workload: str):
         return None
 
 
+def load_issue_ceiling():
+    """The term loop's issue ceiling at measured instruction rates, from the
+    committed microbenchmark summary, or None."""
+    path = os.path.join(PROFILE_DIR, "issue_ceiling.json")
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
+def oracle_threads() -> int:
+    """Threads for the oracle: the host's cores, at most 16 (one GPU's share
+    of its host)."""
+    return min(16, os.cpu_count() or 1)
+
+
 def cpu_baseline(wl, x, w, y_gpu, budget_s: float, profile: str = "hopper"):
     """Time the oracle on whole output rows, sized to about budget_s seconds."""
     import oracle
     orc = oracle.default()
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     xs, ws = x.numpy(), w.numpy()
     sx, sw = scale_bits(wl.scale_x), scale_bits(wl.scale_w)
     # probe the rate on a small sample
@@ -101,6 +134,7 @@ def cpu_baseline(wl, x, w, y_gpu, budget_s: float, profile: str = "hopper"):
     return {"value": ops / dt, "unit": "GEMM-ops/s", "cores": threads, "kind": "oracle",
             "sample": f"output rows 0..{rows - 1} (all {wl.N} columns, K={wl.K}) of the workload, "
                       f"{ops / 2:.3g} MACs in {dt:.1f} s",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "gpu_bit_exact_on_sample": same}
 
 
@@ -124,7 +158,7 @@ def oracle_rates():
     import oracle
     from oracle import spec
     orc = oracle.default()
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     res = {"cpu": cpu_model(), "host_threads": os.cpu_count(), "threads_used": threads}
 
     def timed(fn, min_s=1.0):
@@ -204,6 +238,7 @@ def cpu_baseline_incoming(wl, x, w, c_bits, acc_gpu, budget_s: float, profile: s
     return {"value": ops / dt, "unit": "GEMM-ops/s", "cores": 1, "kind": "oracle",
             "sample": f"output rows 0..{rows - 1} (all {wl.N} columns, K={wl.K}), chains from incoming "
                       f"accumulators, {ops / 2:.3g} MACs in {dt:.1f} s",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "gpu_bit_exact_on_sample": bool(np.array_equal(acc, acc_gpu[:rows]))}
 
 
@@ -229,10 +264,16 @@ def main():
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--oracle-rates", action="store_true",
                     help="only time the CPU oracle (C on 1 and all threads, Python spec on 1) on the host")
+    ap.add_argument("--f4-census", action="store_true",
+                    help="only count, on the host, the blocks an exact int8 matrix-core path could take")
     args = ap.parse_args()
 
     if args.oracle_rates:
         oracle_rates()
+        return
+    if args.f4_census:
+        from bit_exact_fp8_amd import census
+        census.main()
         return
 
     if args.copy_reference:
@@ -274,13 +315,12 @@ def main():
     ws_bytes = api.workspace_bytes(wl.M, wl.N, wl.K, wl.split_S, wl.fast, args.profile)
     wsbuf = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     lib = api._lib()
-    if args.tile >= 0:
-        api.force_tile(args.tile)
+    plan = api.plan_options(tile=args.tile if args.tile >= 0 else None)
     stream = torch.cuda.current_stream(dev)
     call_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
                  wl.M, wl.N, wl.K, sxd.data_ptr(), swd.data_ptr(), None, out.data_ptr(), api.OUT_DTYPE[out.dtype],
                  wl.N, int(wl.fast), wl.split_S, api.PROFILE[args.profile], wsbuf.data_ptr(), ws_bytes,
-                 stream.cuda_stream)
+                 stream.cuda_stream, plan)
 
     def step():
         st = lib.emu_scaled_mm(*call_args)
@@ -294,7 +334,7 @@ def main():
         out = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         cin_args = (xd.data_ptr(), api.FP8_FORMAT[xd.dtype], wl.K, wd.data_ptr(), api.FP8_FORMAT[wd.dtype], wl.K,
                     wl.M, wl.N, wl.K, c_in.data_ptr(), wl.N, out.data_ptr(), wl.N, api.PROFILE[args.profile],
-                    stream.cuda_stream)
+                    stream.cuda_stream, plan)
 
         def step():  # noqa: F811 -- the timed call of this mode
             st = lib.emu_accumulate_c(*cin_args)
@@ -348,12 +388,20 @@ def main():
             "peak": PEAK_ALU / 1e12,
             "unit": "T GEMM-ops/s",
             "frac": achieved / PEAK_ALU,
+            "peak_basis": "VALU issue ceiling of the term loop: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz / "
+                          "2.5 lane-slots per multiply-add x 2",
             "traffic": traffic,
+            "R": R_MODEL / 1e12,
+            "frac_vs_R": achieved / R_MODEL,
             "launch_ms": launch_ms,
             "launch_ms_min": float(np.min(ev_ms)),
             "launch_ms_median": float(np.median(ev_ms)),
         },
     }
+    ceiling = load_issue_ceiling()
+    if ceiling and ceiling.get("gemm_ops_per_s"):
+        result["roofline"]["issue_peak"] = ceiling["gemm_ops_per_s"] / 1e12
+        result["roofline"]["issue_frac"] = achieved / ceiling["gemm_ops_per_s"]
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle on a sample")
         if args.incoming_acc:

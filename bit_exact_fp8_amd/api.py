@@ -7,6 +7,11 @@ There is no CPU fallback: without the built library every call raises.
 ``scaled_mm`` keeps the argument order of ``torch._scaled_mm`` as the mmaemu
 user guide (section 3) describes it: ``mat1`` is ``[M, K]`` row-major, ``mat2``
 is ``[K, N]`` column-major, i.e. ``w.t()`` for a row-major weight ``w [N, K]``.
+
+Every call takes optional plan options for testing and tuning (``tile``: a
+tile configuration index into ``TILE_CONFIGS``; ``defer``: a key of
+``DEFER_MODES``); results never depend on them, and nothing is kept between
+calls.
 """
 from __future__ import annotations
 
@@ -25,6 +30,11 @@ FP8_FORMAT_NAME = {"e4m3fn": 0, "e5m2": 1}
 OUT_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2, torch.float8_e4m3fn: 3,
              torch.float8_e5m2: 4}
 PROFILE = {"hopper": 0, "ada-serial": 1, "ada-pairwise": 2}
+
+
+class PlanOptions(ctypes.Structure):
+    """emu_plan_options of include/emu_fp8gemm.h."""
+    _fields_ = [("tile", ctypes.c_int), ("defer", ctypes.c_int)]
 
 
 class EmuError(RuntimeError):
@@ -52,25 +62,20 @@ def _lib():
             f"{path} is not built: run __graft_entry__.build() (there is no CPU fallback)")
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    opt = ctypes.POINTER(PlanOptions)
     common = [vp, i32, i64, vp, i32, i64, i64, i64, i64]
-    lib.emu_scaled_mm.argtypes = common + [vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.emu_scaled_mm.argtypes = common + [vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, ctypes.c_size_t, vp, opt]
     lib.emu_scaled_mm.restype = i32
-    lib.emu_accumulate.argtypes = common + [vp, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.emu_accumulate.argtypes = common + [vp, i64, i32, i32, i32, vp, ctypes.c_size_t, vp, opt]
     lib.emu_accumulate.restype = i32
-    lib.emu_accumulate_c.argtypes = common + [vp, i64, vp, i64, i32, vp]
+    lib.emu_accumulate_c.argtypes = common + [vp, i64, vp, i64, i32, vp, opt]
     lib.emu_accumulate_c.restype = i32
-    lib.emu_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.emu_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, opt]
     lib.emu_workspace_bytes.restype = ctypes.c_size_t
     lib.emu_status_string.argtypes = [i32]
     lib.emu_status_string.restype = ctypes.c_char_p
     lib.emu_last_error_message.restype = ctypes.c_char_p
     lib.emu_abi_version.restype = i32
-    lib.emu_debug_force_tile.argtypes = [i32]
-    lib.emu_debug_force_tile.restype = i32
-    lib.emu_debug_force_spec.argtypes = [i32]
-    lib.emu_debug_force_spec.restype = i32
-    lib.emu_debug_force_defer.argtypes = [i32]
-    lib.emu_debug_force_defer.restype = i32
     _LIB = lib
     return lib
 
@@ -81,40 +86,21 @@ def abi_version() -> int:
 
 TILE_CONFIGS = ("64x128", "64x64", "32x64", "32x32", "16x16_g2", "16x16_g4", "64x64_mx", "64x128_mx",
                 "16x8_g4", "16x64_mx", "32x32_s4")
-
-
-def force_tile(cfg: int) -> int:
-    """Force the main kernel's tile configuration (index into TILE_CONFIGS,
-    -1 for the automatic choice).  Returns the previous setting."""
-    prev = _lib().emu_debug_force_tile(int(cfg))
-    if prev == -2:
-        raise ValueError(f"invalid tile configuration {cfg}")
-    return prev
-
-
-SPEC_MODES = {"auto": -1, "off": 0, "on": 1, "on-guess-zero": 2, "on-guess-x4": 3}
-
-
-def force_spec(mode: str) -> str:
-    """Force the exponent-speculation plan for fast accumulation (a key of
-    SPEC_MODES).  Returns the previous mode's name."""
-    prev = _lib().emu_debug_force_spec(SPEC_MODES[mode])
-    if prev == -2:
-        raise ValueError(f"invalid speculation mode {mode}")
-    return {v: k for k, v in SPEC_MODES.items()}[prev]
-
-
 DEFER_MODES = {"auto": -1, "off": 0, "on": 1}
 
 
-def force_defer(mode: str) -> str:
-    """Force the deferred-infinity plan (a key of DEFER_MODES: automatic from
-    2^36 multiply-adds, never, or at every size the plan allows).  Returns the
-    previous mode's name."""
-    prev = _lib().emu_debug_force_defer(DEFER_MODES[mode])
-    if prev == -2:
-        raise ValueError(f"invalid deferred-infinity mode {mode}")
-    return {v: k for k, v in DEFER_MODES.items()}[prev]
+def plan_options(tile: int | None = None, defer: str | None = None):
+    """A pointer to emu_plan_options for one call, or None (all automatic).
+    tile: an index into TILE_CONFIGS (None or -1: automatic); defer: a key of
+    DEFER_MODES (the deferred-infinity plan)."""
+    if tile is None and defer is None:
+        return None
+    t = -1 if tile is None else int(tile)
+    if not -1 <= t < len(TILE_CONFIGS):
+        raise ValueError(f"invalid tile configuration {tile}")
+    if defer is not None and defer not in DEFER_MODES:
+        raise ValueError(f"invalid deferred-infinity mode {defer}")
+    return ctypes.pointer(PlanOptions(t, DEFER_MODES[defer or "auto"]))
 
 
 def _check(status: int):
@@ -124,14 +110,20 @@ def _check(status: int):
 
 
 def workspace_bytes(M: int, N: int, K: int, split_S: int = 1, use_fast_accum: bool = True,
-                    profile: str = "hopper") -> int:
-    return int(_lib().emu_workspace_bytes(M, N, K, split_S, int(use_fast_accum), PROFILE[profile]))
+                    profile: str = "hopper", tile: int | None = None, defer: str | None = None) -> int:
+    return int(_lib().emu_workspace_bytes(M, N, K, split_S, int(use_fast_accum), PROFILE[profile],
+                                          plan_options(tile, defer)))
 
 
 def _fmt(t: torch.Tensor) -> int:
     if t.dtype in FP8_FORMAT:
         return FP8_FORMAT[t.dtype]
     raise TypeError(f"expected a float8_e4m3fn or float8_e5m2 tensor, got {t.dtype}")
+
+
+def _on_device(name: str, t: torch.Tensor, device):
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be a CUDA tensor on the operands' device ({device}), not {t.device}")
 
 
 def _scale_ptr(s: torch.Tensor, device) -> int:
@@ -153,11 +145,16 @@ def _operands(mat1, mat2):
     K2, N = mat2.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    if mat1.stride(1) != 1 and M > 1:
-        raise ValueError("mat1 must be row-major [M, K]")
+    # the codes of a row must be contiguous whenever a row holds more than
+    # one (the row stride of a single row is never used)
+    if mat1.stride(1) != 1 and K > 1:
+        raise ValueError("mat1 must be row-major [M, K] (unit stride along K)")
     w = mat2.t()  # [N, K]
-    if w.stride(1) != 1 and N > 1:
+    if w.stride(1) != 1 and K > 1:
         raise ValueError("mat2 must be column-major [K, N] (pass w.t() for a row-major w)")
+    if mat1.device.type != "cuda":
+        raise ValueError(f"the operands must be CUDA tensors, not {mat1.device}")
+    _on_device("mat2", w, mat1.device)
     ldx = mat1.stride(0) if (M > 1 and K > 0) else K
     ldw = w.stride(0) if (N > 1 and K > 0) else K
     return mat1, w, M, N, K, ldx, ldw
@@ -166,13 +163,14 @@ def _operands(mat1, mat2):
 def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
               out_dtype=None, use_fast_accum: bool = False, split_S: int = 1,
               profile: str = "hopper", out: torch.Tensor | None = None,
-              scale_result: torch.Tensor | None = None) -> torch.Tensor:
+              scale_result: torch.Tensor | None = None, tile: int | None = None,
+              defer: str | None = None) -> torch.Tensor:
     """y = (mat1 @ mat2) * scale_a * scale_b with the emulated FP8 arithmetic.
 
     Defaults follow torch (user guide, section 3): use_fast_accum=False and
     out_dtype = the input dtype.  scale_result (FP8 outputs only) is a
     one-element float32 tensor multiplied in before the saturating FP8
-    conversion."""
+    conversion.  tile, defer: plan options (testing and tuning)."""
     x, w, M, N, K, ldx, ldw = _operands(mat1, mat2)
     if out_dtype is None:
         out_dtype = mat1.dtype
@@ -181,31 +179,36 @@ def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, sca
     dev = x.device
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
-    elif out.shape != (M, N) or out.dtype != out_dtype or (N > 1 and out.stride(1) != 1):
-        raise ValueError("out must be a row-major [M, N] tensor of out_dtype")
+    else:
+        _on_device("out", out, dev)
+        if out.shape != (M, N) or out.dtype != out_dtype or (N > 1 and out.stride(1) != 1):
+            raise ValueError("out must be a row-major [M, N] tensor of out_dtype")
     ldo = out.stride(0) if M > 1 else N
-    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
+    plan = plan_options(tile, defer)
+    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile, tile, defer)
     wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     lib = _lib()
     sr = _scale_ptr(scale_result, dev) if scale_result is not None else None
     _check(lib.emu_scaled_mm(x.data_ptr(), _fmt(x), ldx, w.data_ptr(), _fmt(w), ldw, M, N, K,
                              _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), sr, out.data_ptr(),
                              OUT_DTYPE[out_dtype], ldo, int(use_fast_accum), int(split_S),
-                             PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev)))
+                             PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev), plan))
     return out
 
 
 def accumulate(x: torch.Tensor, w: torch.Tensor, use_fast_accum: bool, split_S: int = 1,
-               profile: str = "hopper", c: torch.Tensor | None = None) -> torch.Tensor:
-    """The fp32 accumulator before the epilogue.  Both operands are [rows, K]
-    (user guide, section 3: accumulate takes w, not w.t(), and has no default
-    for use_fast_accum).  c: optional incoming accumulators ([M, N] float32,
+               profile: str = "hopper", c: torch.Tensor | None = None, tile: int | None = None,
+               defer: str | None = None) -> torch.Tensor:
+    """The binary32 accumulator, without the epilogue.  Both operands are
+    [rows, K] (user guide, section 3: this call takes w itself rather than
+    w.t(), and use_fast_accum must be given).  c: optional incoming accumulators ([M, N] float32,
     row-major): the fast chains start from them instead of +0 (fast
-    accumulation and split_S = 1 only)."""
+    accumulation and split_S = 1 only).  tile, defer: plan options."""
     xx, ww, M, N, K, ldx, ldw = _operands(x, w.t())
     dev = xx.device
     acc = torch.empty((M, N), dtype=torch.float32, device=dev)
     ldacc = acc.stride(0) if M > 1 else N
+    plan = plan_options(tile, defer)
     if c is not None:
         if not use_fast_accum or split_S != 1:
             raise EmuError(EMU_ERR_UNSUPPORTED, "incoming accumulators need fast accumulation and split_S = 1")
@@ -214,12 +217,12 @@ def accumulate(x: torch.Tensor, w: torch.Tensor, use_fast_accum: bool, split_S: 
         ldc = c.stride(0) if M > 1 else N
         _check(_lib().emu_accumulate_c(xx.data_ptr(), _fmt(xx), ldx, ww.data_ptr(), _fmt(ww), ldw, M, N, K,
                                        c.data_ptr(), ldc, acc.data_ptr(), ldacc, PROFILE[profile],
-                                       _stream_handle(dev)))
+                                       _stream_handle(dev), plan))
         return acc
-    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile)
+    ws = workspace_bytes(M, N, K, split_S, use_fast_accum, profile, tile, defer)
     wsbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     lib = _lib()
     _check(lib.emu_accumulate(xx.data_ptr(), _fmt(xx), ldx, ww.data_ptr(), _fmt(ww), ldw, M, N, K,
                               acc.data_ptr(), ldacc, int(use_fast_accum), int(split_S),
-                              PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev)))
+                              PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev), plan))
     return acc

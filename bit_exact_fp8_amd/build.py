@@ -1,9 +1,9 @@
 """Build libemu_fp8gemm.so for gfx950 with hipcc (in-tree, next to this file).
 
 The main kernel's variants (block width x format pair) are separate
-translation units of emu_variant.hip (and of emu_spec_variant.hip for the
-exponent-speculation kernels, emu_cin_variant.hip for the chains from
-incoming accumulators), compiled in parallel and linked with the dispatcher,
+translation units of emu_variant.hip (and of emu_cin_variant.hip for the
+chains from incoming accumulators), compiled in parallel and linked with the
+dispatcher,
 the combine kernel, the deferred-infinity kernels (emu_specials.hip) and the
 C ABI."""
 from __future__ import annotations
@@ -40,8 +40,6 @@ def _units(objdir: str):
     for b, xf, wf in VARIANTS:
         defs = [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]
         units.append((os.path.join(CSRC, "emu_variant.hip"), os.path.join(objdir, f"emu_variant_{b}_{xf}{wf}.o"), defs))
-        units.append((os.path.join(CSRC, "emu_spec_variant.hip"), os.path.join(objdir, f"emu_spec_{b}_{xf}{wf}.o"),
-                      defs))
         units.append((os.path.join(CSRC, "emu_cin_variant.hip"), os.path.join(objdir, f"emu_cin_{b}_{xf}{wf}.o"),
                       defs))
     return units

@@ -47,16 +47,6 @@ struct MainParams {
     int64_t split_stride;  // elements between consecutive splits' partials in `out` (S > 1)
     const float *scale_x, *scale_w;
     const float *scale_result;  // FP8 outputs only; null means 1
-    // Exponent speculation (fast accumulation, spec = 1): grid z is
-    // S * chunk_groups as for stored chunks; workgroup z forms the block
-    // words of its range into pk[(split * nbs + block) * M * N + m * N + n],
-    // starting from the guesses guess[z * M * N + m * N + n] that the guess
-    // kernel writes; the walk kernel then runs each chain over the words.
-    int spec;
-    float *guess;
-    uint32_t *pk;
-    int64_t nbs;           // blocks per split in the pk layout
-    int guess_perturb;     // testing: 0 none, 1 range-start guesses 0, 2 four times too large
     // Incoming accumulators (fast accumulation, S = 1): chain (m, n) starts
     // from c_in[m * ldc + n] instead of +0.
     const float *c_in;
@@ -142,12 +132,6 @@ hipError_t launch_main(int cfg, int block, int xfmt, int wfmt, const MainParams 
 // emu_variant.hip.
 template <int BLK, int XF, int WF>
 hipError_t launch_variant(int cfg, const MainParams &p, int S, hipStream_t stream);
-template <int BLK, int XF, int WF>
-hipError_t launch_variant_spec(int which, int cfg, const MainParams &p, int Z, hipStream_t stream);
-// The speculation's guess (which = 0), block-word main kernel (1, tile
-// configuration cfg, grid z = Z) or walk (2) kernel.
-hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const MainParams &p, int Z,
-                       hipStream_t stream);
 template <int BLK, int XF, int WF>
 hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream);
 // The main kernel from incoming accumulators (grid z = 1).

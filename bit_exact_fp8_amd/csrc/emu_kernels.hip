@@ -115,20 +115,6 @@ hipError_t launch_main(int cfg, int block, int xfmt, int wfmt, const MainParams 
     }
 }
 
-hipError_t launch_spec(int which, int cfg, int block, int xfmt, int wfmt, const MainParams &p, int Z, hipStream_t stream)
-{
-    const int key = (block << 4) | (xfmt << 1) | wfmt;
-    switch (key) {
-    case (32 << 4) | 0: return launch_variant_spec<32, 0, 0>(which, cfg, p, Z, stream);
-    case (32 << 4) | 1: return launch_variant_spec<32, 0, 1>(which, cfg, p, Z, stream);
-    case (32 << 4) | 2: return launch_variant_spec<32, 1, 0>(which, cfg, p, Z, stream);
-    case (16 << 4) | 0: return launch_variant_spec<16, 0, 0>(which, cfg, p, Z, stream);
-    case (16 << 4) | 1: return launch_variant_spec<16, 0, 1>(which, cfg, p, Z, stream);
-    case (16 << 4) | 2: return launch_variant_spec<16, 1, 0>(which, cfg, p, Z, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_main_cin(int cfg, int block, int xfmt, int wfmt, const MainParams &p, hipStream_t stream)
 {
     const int key = (block << 4) | (xfmt << 1) | wfmt;

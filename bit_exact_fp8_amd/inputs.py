@@ -84,9 +84,14 @@ WORKLOADS = {
         "mixed_8192", 8192, 8192, 8192, wfmt="e5m2", x_sigma=40.0, w_sigma=1000.0,
         zero_frac=0.01, subnormal_frac=0.01, scale_x=1 / 256, scale_w=1 / 256,
         note="large e4m3 x e5m2 GEMM, 1% zeros and 1% subnormals of both signs"),
+    # the validation page's own bench shape (its results table: the Evo 2 1B
+    # projection at M = 2048), on the user guide's recipe
+    "proj_2048x5760x1920": Workload(
+        "proj_2048x5760x1920", 2048, 5760, 1920,
+        note="the validation page's bench shape, the Evo 2 1B projection at M=2048"),
 }
 WORKLOAD_ORDER = ["tiny", "proj_64x5760x1920", "slow_256x4096x4096", "splitk_16x256x65536_s8",
-                  "mixed_8192"]
+                  "mixed_8192", "proj_2048x5760x1920"]
 
 
 def fp8_codes(values: torch.Tensor, fmt: str) -> torch.Tensor:

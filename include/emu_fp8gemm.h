@@ -14,10 +14,10 @@
  *    largest exponent (field exponents, subnormals at emin), every term is cut
  *    toward zero to 13 fraction bits, and the block sum is cut toward zero to
  *    14 significant bits; a zero block result is +0.
- *  - fast_accum != 0 chains the blocks along K; fast_accum == 0 restarts the
- *    chain every 128 K and adds the chunk results in K order in binary32
- *    round-to-nearest-even.
- *  - split_S > 1 splits K into contiguous runs of 128-wide k-tiles,
+ *  - fast_accum != 0 chains the blocks along K; fast_accum == 0 starts a new
+ *    chain at every 128th position of K and sums the chunk results, first
+ *    chunk first, with binary32 round-to-nearest-even additions.
+ *  - split_S > 1 splits K into runs of consecutive 128-wide k-tiles,
  *    ceil(ceil(K/128)/S) tiles per split (trailing splits may be empty and
  *    give +0), and adds the partials serially, p0 + p1 + ... in binary32.
  *  - the epilogue is alpha = RN32(scale_x * scale_w), y32 = RN32(acc*alpha+(+0))
@@ -27,11 +27,11 @@
  *    saturate: |y'| at or above the format's largest finite value (448 for
  *    e4m3fn, 57344 for e5m2), infinities included, becomes that value
  *    (validation page, scope table row "Epilogue" and claims table).
- *  - a NaN code anywhere in row m of x or row n of w makes output (m, n) the
- *    canonical NaN (0x7FFFFFFF for fp32, 0x7FFF for bf16/fp16, 0x7F for FP8;
- *    the bit patterns are a reading: the pages say "canonical" only).  E5M2
- *    infinities follow IEEE: Inf*0 or infinite products of both signs give
- *    NaN, otherwise the signed infinity.
+ *  - an output (m, n) whose x row m or w row n holds a NaN code anywhere is
+ *    the canonical NaN (0x7FFFFFFF for fp32, 0x7FFF for bf16/fp16, 0x7F for
+ *    FP8; the bit patterns are a reading: the pages say "canonical" only).
+ *    E5M2 infinities follow IEEE: Inf*0 or infinite products of both signs
+ *    give NaN, otherwise the signed infinity.
  *
  * Layouts (all pointers are device pointers owned by the caller):
  *   x   [M, K] row-major FP8 codes, leading dimension ldx (bytes >= K);
@@ -45,7 +45,8 @@
  * returns; it never synchronises and never allocates device memory.  The
  * caller keeps all buffers alive until the stream has run the work.  `out`
  * is fully overwritten and never read.  Results are deterministic: no
- * atomics take part in the arithmetic.
+ * atomics take part in the arithmetic.  The library keeps no mutable state
+ * between calls other than the thread-local error text.
  *
  * Errors: arguments are checked on the host before anything is enqueued; a
  * non-OK status means nothing was written.  emu_last_error_message() gives
@@ -57,11 +58,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define EMU_ABI_VERSION 4
+#define EMU_ABI_VERSION 5
 
 #if defined(EMU_BUILDING_LIBRARY)
 #define EMU_API __attribute__((visibility("default")))
@@ -71,7 +74,8 @@ extern "C" {
 
 typedef enum {
     EMU_OK = 0,
-    EMU_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad leading dimension, unknown enum, split_S < 1 */
+    EMU_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad leading dimension, unknown enum, split_S < 1,
+                                plan options out of range */
     EMU_ERR_REJECTED = 2,    /* a call torch 2.7.1 / cuBLASLt would reject (limitations page, features table;
                                 validation page, claims table): e5m2 x e5m2, e4m3fn x e4m3fn -> e5m2,
                                 K or N not a multiple of 16, x / w / out not 16-byte aligned,
@@ -98,11 +102,11 @@ typedef enum {
 /* The arithmetic profile (user guide section 4: profiles name a reference
  * platform; hopper is the default).
  *   EMU_PROFILE_HOPPER: the H100 PCIe -- 32-product blocks; split_S > 1 cuts
- *     K into contiguous runs of 128-wide k-tiles (ceil layout), partials
+ *     K into runs of consecutive 128-wide k-tiles (ceil layout), partials
  *     added serially.
  *   EMU_PROFILE_ADA_SERIAL / EMU_PROFILE_ADA_PAIRWISE: the RTX 4060 --
  *     16-product blocks (validation page, scope table row "Ada instruction
- *     model"); split_S > 1 deals 64-wide k-tiles round-robin to the splits
+ *     model"); split_S > 1 deals 64-wide k-tiles to the splits in turn
  *     (tile t to split t mod S), each split chains (and, for slow
  *     accumulation, restarts every 128) along its own tiles in order, and
  *     the partials are added serially or by the pairwise tree (limitations
@@ -118,6 +122,31 @@ typedef enum {
     EMU_PROFILE_ADA_PAIRWISE = 2
 } emu_profile;
 
+/* Tile configurations of the main kernel (output rows x columns per
+ * workgroup; results never depend on the configuration). */
+#define EMU_TILE_AUTO (-1)
+#define EMU_TILE_COUNT 11
+
+/*
+ * Plan options, for testing and tuning; a NULL pointer means every field at
+ * its automatic value.  Results do not depend on them.
+ *   tile:  EMU_TILE_AUTO, or 0 .. EMU_TILE_COUNT-1 to force the main
+ *          kernel's tile configuration: 64x128, 64x64, 32x64, 32x32 output
+ *          tiles with one lane per output; 16x16 with 2 or 4 lanes per
+ *          output; 64x64 and 64x128 with the block exponent maxima on the
+ *          matrix cores; 16x8 with 4 lanes per output; 16x64 with
+ *          matrix-core maxima in one wave; 32x32 staging 4 K-blocks per
+ *          barrier.
+ *   defer: the deferred-infinity plan described at emu_workspace_bytes:
+ *          -1 automatic (from 2^36 multiply-adds), 0 never, 1 at every size
+ *          the plan allows.  Changes emu_workspace_bytes.
+ * Any other value returns EMU_ERR_INVALID_ARG (emu_workspace_bytes: 0).
+ */
+typedef struct {
+    int tile;
+    int defer;
+} emu_plan_options;
+
 /*
  * y = (x @ w.T) * scale_x * scale_w (torch._scaled_mm semantics with
  * tensor-wise scales; user guide section 3).
@@ -129,33 +158,36 @@ typedef enum {
  * M >= 0 (any value), N >= 0 and K >= 0 multiples of 16.  M = 0 or N = 0
  * returns EMU_OK without enqueuing anything; K = 0 writes +0 everywhere.
  * workspace: device memory of emu_workspace_bytes(M, N, K, split_S,
- * fast_accum, profile) bytes (may be NULL when that is 0), 4-byte aligned;
- * its contents on entry do not matter.  Only the split partials, stored
- * chunk results and speculation arrays are required (a smaller workspace
- * returns EMU_ERR_WORKSPACE); without the optional infinity lists at its end
- * the call is still bit-exact, only slower on large inputs whose e5m2 rows
- * hold infinities.  stream: a hipStream_t (NULL = the default stream).
+ * fast_accum, profile, plan) bytes (may be NULL when that is 0), 4-byte
+ * aligned; its contents on entry do not matter.  Only the split partials and
+ * stored chunk results are required (a smaller workspace returns
+ * EMU_ERR_WORKSPACE); without the optional infinity lists at its end the
+ * call is still bit-exact, only slower on large inputs whose e5m2 rows hold
+ * infinities.  stream: the HIP stream to enqueue on (NULL = the default
+ * stream).  plan: NULL, or plan options (above).
  */
 EMU_API emu_status emu_scaled_mm(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
-                         const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
-                         int64_t M, int64_t N, int64_t K,
-                         const float *scale_x, const float *scale_w, const float *scale_result,
-                         void *out, emu_out_dtype out_dtype, int64_t ldo,
-                         int fast_accum, int split_S, emu_profile profile,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                                 const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
+                                 int64_t M, int64_t N, int64_t K,
+                                 const float *scale_x, const float *scale_w, const float *scale_result,
+                                 void *out, emu_out_dtype out_dtype, int64_t ldo,
+                                 int fast_accum, int split_S, emu_profile profile,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                 const emu_plan_options *plan);
 
 /*
  * The binary32 accumulator before the epilogue: acc [M, N] row-major with
  * leading dimension ldacc (mmaemu's accumulate(x, w, use_fast_accum), user
  * guide section 3).  NaN results are 0x7FFFFFFF.  Same rules for the
- * operands, workspace and stream as emu_scaled_mm.
+ * operands, workspace, stream and plan as emu_scaled_mm.
  */
 EMU_API emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
-                          const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
-                          int64_t M, int64_t N, int64_t K,
-                          float *acc, int64_t ldacc,
-                          int fast_accum, int split_S, emu_profile profile,
-                          void *workspace, size_t workspace_bytes, void *stream);
+                                  const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
+                                  int64_t M, int64_t N, int64_t K,
+                                  float *acc, int64_t ldacc,
+                                  int fast_accum, int split_S, emu_profile profile,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                  const emu_plan_options *plan);
 
 /*
  * Fast accumulation from incoming accumulators: acc[m, n] is the fast chain
@@ -174,21 +206,18 @@ EMU_API emu_status emu_accumulate(const uint8_t *x, emu_fp8_format x_fmt, int64_
  * c_in [M, N] row-major with leading dimension ldc, acc [M, N] with ldacc
  * (elements; device memory, 4-byte aligned); acc may be c_in itself (each
  * element is read before its output is written).  No workspace.  Operand
- * rules and errors as emu_accumulate.
+ * rules and errors as emu_accumulate; plan.defer is not used.
  */
 EMU_API emu_status emu_accumulate_c(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
                                     const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
                                     int64_t M, int64_t N, int64_t K,
                                     const float *c_in, int64_t ldc, float *acc, int64_t ldacc,
-                                    emu_profile profile, void *stream);
+                                    emu_profile profile, hipStream_t stream, const emu_plan_options *plan);
 
 /* Device workspace in bytes for emu_scaled_mm and emu_accumulate with these
- * arguments (0 for invalid sizes).  Required: split partials
- * (split_S * M * N * 4 when split_S > 1), the results of groups of 128-K
- * chunks when slow accumulation over a small output grid stores them, or,
- * for fast accumulation over a small output grid with long chains (when
- * forced), the exponent-speculation arrays (one 4-byte word per 32 or 16
- * products of every output, plus one guess per output and K range).
+ * arguments (0 for invalid sizes or plan options).  Required: split partials
+ * (split_S * M * N * 4 when split_S > 1), or the results of groups of 128-K
+ * chunks when slow accumulation over a small output grid stores them.
  * Optional, at the end: on problems of M * N * K >= 2^36 with K <= 64496
  * that store no chunk results, the infinity lists, 65 * 4 bytes per row of
  * the larger of M and N (e5m2 operands only use them): a pass over the e5m2
@@ -196,7 +225,7 @@ EMU_API emu_status emu_accumulate_c(const uint8_t *x, emu_fp8_format x_fmt, int6
  * outputs those rows make non-finite, and a fix-up kernel resolves them from
  * the lists.  Depends on the plan only, never on the data or formats. */
 EMU_API size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum,
-                           emu_profile profile);
+                                   emu_profile profile, const emu_plan_options *plan);
 
 /* Static description of a status code. */
 EMU_API const char *emu_status_string(emu_status status);
@@ -210,42 +239,6 @@ EMU_API const char *emu_last_error_message(void);
 EMU_API int emu_abi_version(void);
 
 /*
- * Testing and tuning: force the main kernel's tile configuration for every
- * later call in the process (cfg = -1 restores the automatic choice; valid
- * configurations are 0 .. 10: 64x128, 64x64, 32x64, 32x32 output tiles with
- * one lane per output, 16x16 with 2 or 4 lanes per output, 64x64 and
- * 64x128 with the block exponent maxima on the matrix cores, 16x8 with 4
- * lanes per output, 16x64 with matrix-core maxima in one wave, 32x32
- * staging 4 K-blocks per barrier).  Results do not
- * depend on the configuration.  Returns the previous setting, or -2 (and
- * changes nothing) for an invalid cfg.  Process-wide; not for concurrent use
- * with calls that expect the automatic choice.
- */
-EMU_API int emu_debug_force_tile(int cfg);
-
-/*
- * Testing and tuning: force the exponent-speculation plan for fast
- * accumulation (mode -1: automatic; 0: never; 1: whenever the forced or
- * automatic tile allows it; 2, 3: as 1, with the guesses at the start of
- * every K range replaced by 0 (2) or by four times their value (3), so that
- * many blocks take the exact recomputation).  Results do not depend on the
- * mode.  The mode also changes emu_workspace_bytes.  Returns the previous
- * mode, or -2 (and changes nothing) for an invalid mode.  Process-wide, like
- * emu_debug_force_tile.
- */
-EMU_API int emu_debug_force_spec(int mode);
-
-/*
- * Testing and tuning: force the deferred-infinity plan described at
- * emu_workspace_bytes (mode -1: automatic, from 2^36 multiply-adds; 0:
- * never; 1: at every size the plan allows).  Results do not depend on the
- * mode.  The mode also changes emu_workspace_bytes.  Returns the previous
- * mode, or -2 (and changes nothing) for an invalid mode.  Process-wide, like
- * emu_debug_force_tile.
- */
-EMU_API int emu_debug_force_defer(int mode);
-
-/*
  * Host builds of the library's own IEEE rounding routines, the same source
  * its kernels use, exported so that CPU tests can check them without a GPU.
  * All arguments and results are bit patterns.
@@ -256,10 +249,6 @@ EMU_API int emu_debug_force_defer(int mode);
  *   emu_host_f32_to_e4m3fn / emu_host_f32_to_e5m2: round to nearest even,
  *       subnormals kept, saturation to +-448 / +-57344 (infinities
  *       included), NaN -> 0x7F.
- *   emu_host_block_step: one block step of the accumulation (host memory):
- *       the products x[i] * w[i], i < n <= 32, of finite FP8 codes, with the
- *       incoming binary32 accumulator c (at most 14 significant bits, or +0);
- *       returns the new accumulator, or 0xFFFFFFFF for invalid arguments.
  */
 EMU_API uint32_t emu_host_mul_f32(uint32_t a, uint32_t b);
 EMU_API uint32_t emu_host_epilogue_f32(uint32_t acc, uint32_t alpha);
@@ -267,7 +256,6 @@ EMU_API uint16_t emu_host_f32_to_bf16(uint32_t f);
 EMU_API uint16_t emu_host_f32_to_f16(uint32_t f);
 EMU_API uint8_t emu_host_f32_to_e4m3fn(uint32_t f);
 EMU_API uint8_t emu_host_f32_to_e5m2(uint32_t f);
-EMU_API uint32_t emu_host_block_step(uint32_t c, const uint8_t *x, int x_fmt, const uint8_t *w, int w_fmt, int n);
 
 #ifdef __cplusplus
 }
