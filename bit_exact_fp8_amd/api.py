@@ -70,6 +70,8 @@ def _lib():
     lib.emu_accumulate.restype = i32
     lib.emu_accumulate_c.argtypes = common + [vp, i64, vp, i64, i32, vp, opt]
     lib.emu_accumulate_c.restype = i32
+    lib.emu_scaled_mm_noalloc.argtypes = common + [vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, opt]
+    lib.emu_scaled_mm_noalloc.restype = i32
     lib.emu_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, opt]
     lib.emu_workspace_bytes.restype = ctypes.c_size_t
     lib.emu_status_string.argtypes = [i32]
@@ -193,6 +195,32 @@ def scaled_mm(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, sca
                              _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), sr, out.data_ptr(),
                              OUT_DTYPE[out_dtype], ldo, int(use_fast_accum), int(split_S),
                              PROFILE[profile], wsbuf.data_ptr(), ws, _stream_handle(dev), plan))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # EMU_NOALLOC_SCRATCH_BYTES
+
+
+def scaled_mm_noalloc(mat1: torch.Tensor, mat2: torch.Tensor, scale_a: torch.Tensor, scale_b: torch.Tensor,
+                      out: torch.Tensor, use_fast_accum: bool = False, split_S: int = 1,
+                      profile: str = "hopper", scale_result: torch.Tensor | None = None,
+                      tile: int | None = None, defer: str | None = None) -> torch.Tensor:
+    """scaled_mm through emu_scaled_mm_noalloc, for callers that cannot
+    allocate device memory: the caller gives the output tensor (its dtype is
+    the output type), and the library's fixed per-GPU scratch takes the place
+    of the workspace.  Calls on one GPU that may overlap share that scratch
+    and must be ordered by the caller."""
+    x, w, M, N, K, ldx, ldw = _operands(mat1, mat2)
+    dev = x.device
+    _on_device("out", out, dev)
+    if out.shape != (M, N) or out.dtype not in OUT_DTYPE or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a row-major [M, N] tensor of a supported output dtype")
+    ldo = out.stride(0) if M > 1 else N
+    sr = _scale_ptr(scale_result, dev) if scale_result is not None else None
+    _check(_lib().emu_scaled_mm_noalloc(x.data_ptr(), _fmt(x), ldx, w.data_ptr(), _fmt(w), ldw, M, N, K,
+                                        _scale_ptr(scale_a, dev), _scale_ptr(scale_b, dev), sr, out.data_ptr(),
+                                        OUT_DTYPE[out.dtype], ldo, int(use_fast_accum), int(split_S),
+                                        PROFILE[profile], _stream_handle(dev), plan_options(tile, defer)))
     return out
 
 

@@ -3,8 +3,8 @@
 The main kernel's variants (block width x format pair) are separate
 translation units of emu_variant.hip (and of emu_cin_variant.hip for the
 chains from incoming accumulators), compiled in parallel and linked with the
-dispatcher,
-the combine kernel, the deferred-infinity kernels (emu_specials.hip) and the
+dispatcher, the combine kernel, the deferred-infinity kernels
+(emu_specials.hip), the no-allocation entry point (emu_noalloc.hip) and the
 C ABI."""
 from __future__ import annotations
 
@@ -36,6 +36,7 @@ VARIANTS = [(b, xf, wf) for b in (32, 16) for xf, wf in ((0, 0), (0, 1), (1, 0))
 def _units(objdir: str):
     units = [(os.path.join(CSRC, "emu_kernels.hip"), os.path.join(objdir, "emu_kernels.o"), []),
              (os.path.join(CSRC, "emu_specials.hip"), os.path.join(objdir, "emu_specials.o"), []),
+             (os.path.join(CSRC, "emu_noalloc.hip"), os.path.join(objdir, "emu_noalloc.o"), []),
              (os.path.join(CSRC, "emu_api.cpp"), os.path.join(objdir, "emu_api.o"), [])]
     for b, xf, wf in VARIANTS:
         defs = [f"-DEMU_VARIANT_BLK={b}", f"-DEMU_VARIANT_XF={xf}", f"-DEMU_VARIANT_WF={wf}"]

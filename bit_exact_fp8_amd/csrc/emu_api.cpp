@@ -413,6 +413,43 @@ emu_status scaled_mm_call(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, c
 
 }  // namespace
 
+namespace emu {
+
+emu_status scaled_mm_in_scratch(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
+                                emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                                const float *scale_x, const float *scale_w, const float *scale_result, void *out,
+                                emu_out_dtype out_dtype, int64_t ldo, int fast_accum, int split_S,
+                                emu_profile profile, void *(*scratch)(size_t *bytes, std::string *err),
+                                size_t scratch_bytes, hipStream_t stream, const emu_plan_options *plan)
+{
+    // the same checks as emu_scaled_mm, then the required part of the plan
+    // (stored chunk results capped at the scratch size) against the scratch,
+    // before the scratch is looked up
+    emu_status s = check_common(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, split_S, profile);
+    if (s != EMU_OK) return s;
+    const emu_plan_options opt = options_of(plan);
+    if (!options_valid(opt)) return fail(EMU_ERR_INVALID_ARG, "plan options out of range");
+    if (M > 0 && N > 0) {
+        const Plan pl = make_plan(profile, M, N, K, split_S, fast_accum, opt, (int64_t)scratch_bytes);
+        if ((size_t)pl.required_bytes() > scratch_bytes)
+            return fail(EMU_ERR_WORKSPACE, "the split partials need " + std::to_string(pl.required_bytes()) +
+                                               " bytes, more than the " + std::to_string(scratch_bytes) +
+                                               "-byte scratch of the no-allocation entry point");
+    }
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (M > 0 && N > 0) {
+        std::string err;
+        ws = scratch(&ws_bytes, &err);
+        if (!ws) return fail(EMU_ERR_DEVICE, err);
+    }
+    return scaled_mm_call(x, x_fmt, ldx, w, w_fmt, ldw, M, N, K, scale_x, scale_w, scale_result, out,
+                          (int)out_dtype < 0 ? 1000 : (int)out_dtype, ldo, fast_accum, split_S, profile, ws,
+                          ws_bytes, stream, plan, (int64_t)scratch_bytes);
+}
+
+}  // namespace emu
+
 extern "C" {
 
 size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum, emu_profile profile,

@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "../../include/emu_fp8gemm.h"
+
 namespace emu {
 
 // What the main kernel writes for each output.
@@ -141,5 +145,18 @@ hipError_t launch_combine(const CombineParams &p, hipStream_t stream);
 // fix-up kernel.
 hipError_t launch_inf_rows(const DeferParams &p, hipStream_t stream);
 hipError_t launch_inf_fixup(const DeferParams &p, hipStream_t stream);
+
+// emu_scaled_mm with a fixed device scratch of scratch_bytes in place of the
+// caller's workspace: the same checks, a plan whose required part fits the
+// scratch (slow-mode chunk results are stored only when they fit; split
+// partials that do not fit return EMU_ERR_WORKSPACE), then scratch() for the
+// current device's scratch address (nullptr and a message on failure), then
+// the same launches.  No device memory is allocated.
+emu_status scaled_mm_in_scratch(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx, const uint8_t *w,
+                                emu_fp8_format w_fmt, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                                const float *scale_x, const float *scale_w, const float *scale_result, void *out,
+                                emu_out_dtype out_dtype, int64_t ldo, int fast_accum, int split_S,
+                                emu_profile profile, void *(*scratch)(size_t *bytes, std::string *err),
+                                size_t scratch_bytes, hipStream_t stream, const emu_plan_options *plan);
 
 }  // namespace emu

@@ -227,6 +227,36 @@ EMU_API emu_status emu_accumulate_c(const uint8_t *x, emu_fp8_format x_fmt, int6
 EMU_API size_t emu_workspace_bytes(int64_t M, int64_t N, int64_t K, int split_S, int fast_accum,
                                    emu_profile profile, const emu_plan_options *plan);
 
+/* Bytes of the device scratch that emu_scaled_mm_noalloc uses per GPU. */
+#define EMU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * emu_scaled_mm without a workspace argument.  Its split partials, stored
+ * slow-mode chunk results and infinity lists live in a fixed array of
+ * EMU_NOALLOC_SCRATCH_BYTES (64 MiB) in the library's device memory, one
+ * copy per GPU, held until the process ends; the call allocates nothing (the
+ * array's address is looked up once per device, on the first call with that
+ * device current).  Arguments, results and errors are those of
+ * emu_scaled_mm, on the current device, which must be the stream's.  Plans
+ * whose required part does not fit the scratch: slow accumulation stores
+ * its chunk results only when they fit (the results are the same either
+ * way); split partials beyond it, split_S * M * N * 4 bytes above
+ * EMU_NOALLOC_SCRATCH_BYTES, return EMU_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's scratch: calls that may
+ * run at the same time on one GPU (other streams, other threads) race and
+ * must be ordered by the caller; the scratch needs no clearing between
+ * calls.
+ */
+EMU_API emu_status emu_scaled_mm_noalloc(const uint8_t *x, emu_fp8_format x_fmt, int64_t ldx,
+                                         const uint8_t *w, emu_fp8_format w_fmt, int64_t ldw,
+                                         int64_t M, int64_t N, int64_t K,
+                                         const float *scale_x, const float *scale_w, const float *scale_result,
+                                         void *out, emu_out_dtype out_dtype, int64_t ldo,
+                                         int fast_accum, int split_S, emu_profile profile,
+                                         hipStream_t stream, const emu_plan_options *plan);
+
 /* Static description of a status code. */
 EMU_API const char *emu_status_string(emu_status status);
 
