@@ -188,16 +188,28 @@ __device__ __forceinline__ int dot2_i16(uint32_t a, uint32_t b, int c)
     return __builtin_amdgcn_sdot2(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b), c, false);
 }
 
-// Exchange with the partner lane inside each quad: lane ^ 1 (quad_perm
-// [1,0,3,2]) and lane ^ 2 (quad_perm [2,3,0,1]).
-__device__ __forceinline__ uint32_t quad_xor1(uint32_t v)
+// max(v, v of the partner lane) on the low 16 bits, and v + v of the partner
+// lane, for the quad DPP patterns 0xB1 (lane ^ 1) and 0x4E (lane ^ 2): each
+// one DPP-modified instruction (v_max_u16_dpp, v_add_u32_dpp).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_max_lo16(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+    return __builtin_elementwise_max((unsigned short)v, (unsigned short)o);
 }
 
-__device__ __forceinline__ uint32_t quad_xor2(uint32_t v)
+template <int CTRL>
+__device__ __forceinline__ int quad_add(int v)
 {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// The sign pair (+-1, +-1) of two products from the packed 16-bit sign masks
+// of their x and w codes (0xFFFF negative, 0 positive): (sa ^ sb) | 1 per
+// half, one v_bitop3_b32 (truth table 0xBE: (a ^ b) | c).
+__device__ __forceinline__ uint32_t sign_pair(uint32_t sa, uint32_t sb)
+{
+    return __builtin_amdgcn_bitop3_b32(sa, sb, 0x00010001u, 0xBE);
 }
 
 // ---- floating-point mode control -----------------------------------------
@@ -264,6 +276,21 @@ __device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t to
         "v_mad_i32_i16 %0, %2, %1, 0"
         : "=v"(acc), "=&v"(sgn), "=&v"(r)
         : "v"(c), "v"(Cb), "s"(tok));
+    return acc;
+}
+
+// The same term where G lanes share a chain and it enters the block sum on
+// one lane only: that lane clamps c's bits to [lo, hi] = [-1, 1], the others
+// to [0, 0], so their term is 0 without a separate select.
+__device__ __forceinline__ int c_block_term_on(uint32_t c, uint32_t Cb, uint32_t tok, int lo, int hi)
+{
+    int acc;
+    uint32_t sgn, r;
+    asm("v_med3_i32 %1, %3, %6, %7\n\t"
+        "v_fma_f32 %2, |%3|, 1.0, %4\n\t"
+        "v_mad_i32_i16 %0, %2, %1, 0"
+        : "=v"(acc), "=&v"(sgn), "=&v"(r)
+        : "v"(c), "v"(Cb), "s"(tok), "v"(lo), "v"(hi));
     return acc;
 }
 
@@ -626,6 +653,11 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr int K4PL = BLK / 4 / G;      // groups of 4 products per lane and block
     static_assert(WPL % WU == 0 && K4PL >= 1, "block slice per lane");
     static_assert(SS >= 1 && (!MX || SS == 1), "stages per barrier: matrix-core exponents use one");
+    // Unroll of the per-block pass loops: whole blocks for thread tiles of
+    // at most 4 outputs (immediate LDS offsets), except the two-stage 2x2
+    // tile, whose four waves per SIMD would then spill registers (it keeps
+    // an unroll of 2); none for larger thread tiles (registers).
+    constexpr int PASS_UNROLL = (RM * RN > 4) ? 1 : (SS == 2 && RM * RN == 4) ? 2 : 8;
     // CIN: fast accumulation from incoming accumulators c_in instead of +0
     constexpr bool CIN = ACC == ACC_FAST_CIN;
     constexpr bool FAST = ACC == ACC_FAST || CIN, CHUNKS = ACC == ACC_SLOW_CHUNKS;
@@ -647,6 +679,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 
     const int t = threadIdx.x;
     const int lane_g = t % G, slot = t / G;
+    const int c_lo = lane_g == 0 ? -1 : 0, c_hi = lane_g == 0 ? 1 : 0;  // see c_block_term_on
     const int tn = slot % TN, tm = slot / TN;
     const int wave = t >> 6, lane = t & 63;
     // local row of chain i, local column of chain j
@@ -663,7 +696,6 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     const int split = RANGED ? blockIdx.z / p.chunk_groups : blockIdx.z;
     const int group = RANGED ? blockIdx.z % p.chunk_groups : 0;
     const SplitSeq sq = split_seq(p, split);
-    const int64_t tile_mask = (int64_t(1) << p.tile_shift) - 1;
     // positions [pos_begin, pos_end) of the split's k-list: all of them, or
     // one group of 128-chunks when chunk results are stored
     const int64_t span = (int64_t)p.chunks_per_group * CHUNK;
@@ -681,32 +713,44 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     // Stages at sequence positions pos, pos + 32, ..., pos + 32*(SS-1) (each a
     // multiple of 32 inside one k-tile): chunk idx = t + q*NT is stage
     // idx / NCHUNK, row (idx % NCHUNK) >> 1 (x rows first), half idx & 1.
-    // k runs from sq.k_of(stage position) up to the end of that tile or of
-    // K; codes past it, and stages past the k-list, load as zeros (zero
-    // products: neutral in every block).
+    // A 32-wide stage never straddles a k-tile (tiles are 64 or 128 wide and
+    // stages start at multiples of 32 of the k-list), and only the last
+    // k-tile of K can be short, so a chunk is loaded when its k is below K;
+    // codes past K, rows past M or N and stages past the k-list load as
+    // zeros (zero products: neutral in every block).  Each thread's row
+    // pointers (with its 16-byte half) and stage offsets are fixed for the
+    // whole walk: small thread tiles keep them in registers, large ones
+    // (whose register budget is tight) recompute them at every load.
+    constexpr bool KEEP_ROWS = RM * RN <= 4;
+    auto chunk_row_of = [&](int q) -> const uint8_t * {
+        const int idx = t + q * NT;
+        const int c = idx % NCHUNK, r = c >> 1;
+        const uint8_t *row = nullptr;
+        if (idx < NCHUNK * SS) {
+            if (r < BM) {
+                if (m0 + r < p.M) row = p.x + (m0 + r) * p.ldx;
+            } else if (n0 + (r - BM) < p.N) {
+                row = p.w + (n0 + r - BM) * p.ldw;
+            }
+        }
+        return row ? row + 16 * (c & 1) : nullptr;
+    };
+    const uint8_t *chunk_row[KEEP_ROWS ? CPT : 1];
+    if constexpr (KEEP_ROWS) {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) chunk_row[q] = chunk_row_of(q);
+    }
     auto load_block = [&](int64_t pos) {
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
+            const int half = 16 * (idx & 1);
             raw[q] = make_uint4(0, 0, 0, 0);
-            if (idx < NCHUNK * SS) {
-                const int st = idx / NCHUNK, c = idx % NCHUNK;
-                const int r = c >> 1, half = c & 1;
-                const int64_t sp = pos + (int64_t)st * KB;
-                if (sp < pos_end) {
-                    const int64_t kb = sq.k_of(sp);
-                    const int64_t tile_end = kb - (sp & tile_mask) + tile_mask + 1;
-                    const int64_t lim = tile_end < p.K ? tile_end : p.K;
-                    const int64_t k = kb + 16 * half;
-                    if (k < lim) {
-                        if (r < BM) {
-                            if (m0 + r < p.M)
-                                raw[q] = *reinterpret_cast<const uint4 *>(p.x + (m0 + r) * p.ldx + k);
-                        } else if (n0 + (r - BM) < p.N) {
-                            raw[q] = *reinterpret_cast<const uint4 *>(p.w + (n0 + r - BM) * p.ldw + k);
-                        }
-                    }
-                }
+            const int64_t sp = pos + (int64_t)(idx / NCHUNK) * KB;
+            const uint8_t *row = KEEP_ROWS ? chunk_row[KEEP_ROWS ? q : 0] : chunk_row_of(q);
+            if (row && sp < pos_end) {
+                const int64_t k = sq.k_of(sp);
+                if (k + half < p.K) raw[q] = *reinterpret_cast<const uint4 *>(row + k);
             }
         }
     };
@@ -796,7 +840,11 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
         // prefetch the next stages; latency hidden by the compute below
         if (pos + (int64_t)KB * SS < pos_end) load_block(pos + (int64_t)KB * SS);
 
-#pragma unroll 1
+        // all the stages of one barrier unrolled: every LDS address of the
+        // stage's planes is then a per-thread base plus an immediate offset
+        // (not for two stages of 2x2 thread tiles: unrolled, their four
+        // waves per SIMD would spill registers)
+#pragma unroll((SS == 2 && RM * RN == 4) ? 1 : SS)
         for (int st = 0; st < SS; ++st) {
         const int64_t spos = pos + (int64_t)st * KB;
         if (spos >= pos_end) break;  // uniform across the workgroup
@@ -846,7 +894,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 for (int i = 0; i < RM; ++i)
 #pragma unroll
                     for (int j = 0; j < RN; ++j) gmax[i][j] = 0u;
-#pragma unroll(RM * RN <= 4 ? 2 : 1)
+#pragma unroll(PASS_UNROLL)
                 for (int wo = hb * WPB + lane_g * WPL; wo < hb * WPB + (lane_g + 1) * WPL; wo += WU) {
                     if constexpr (WU == 4) {
                         uint4 ea[RM], eb[RN];
@@ -882,40 +930,33 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     }
                 }
 
-                if (G >= 2) {
-#pragma unroll
-                    for (int i = 0; i < RM; ++i)
-#pragma unroll
-                        for (int j = 0; j < RN; ++j) {
-                            uint32_t g = gmax[i][j];
-                            if (G == 2) g = pk_max3_h(g, quad_xor1(g), g);
-                            if (G == 4) g = pk_max3_h(g, quad_xor1(g), quad_xor2(g));
-                            if (G == 4) g = pk_max3_h(g, quad_xor1(g), g);
-                            gmax[i][j] = g;
-                        }
-                }
-
-                // block prologue: C and the truncated incoming accumulator
+                // block prologue: C and the truncated incoming accumulator.
+                // The maximum of this lane's two plane halves and c's
+                // exponent (every lane of a chain carries the same c), then
+                // over the G lanes of the chain; only its low 9 bits reach C.
 #pragma unroll
                 for (int i = 0; i < RM; ++i)
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
-                        const uint32_t g = gmax[i][j];
                         const uint32_t ec = ((c[i][j] >> 23) & 0xFFu) | SUM_OFFSET;
-                        // only the low 9 bits of the maximum reach C
-                        uint32_t cb = (max3_lo_hi_u16(g, ec) << 23) + C_OFFSET;
+                        uint32_t e = max3_lo_hi_u16(gmax[i][j], ec);
+                        if (G >= 2) e = quad_max_lo16<0xB1>(e);
+                        if (G == 4) e = quad_max_lo16<0x4E>(e);
+                        uint32_t cb = (e << 23) + C_OFFSET;
                         asm("" : "+v"(cb));  // later uses derive from C itself
                         Cb[i][j] = cb;
-                        const int ct = c_block_term(c[i][j], Cb[i][j], tok);
-                        acc[i][j] = (G == 1 || lane_g == 0) ? ct : 0;  // c enters the block sum once
+                        // c enters the block sum once
+                        acc[i][j] = (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok)
+                                             : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             }
 
             // pass 2: truncated terms, signs, accumulation (small thread tiles
-            // unroll twice, so the next LDS reads overlap this iteration's
-            // arithmetic: they run at 1-2 waves per SIMD)
-#pragma unroll(RM * RN <= 4 ? 2 : 1)
+            // unroll the whole block: its LDS reads then take immediate
+            // offsets from one address per plane, and the reads of later
+            // steps can overlap earlier arithmetic at 1-2 waves per SIMD)
+#pragma unroll(PASS_UNROLL)
             for (int k4 = hb * (BLK / 4) + lane_g * K4PL; k4 < hb * (BLK / 4) + (lane_g + 1) * K4PL; ++k4) {
                 float4 av[RM], bv[RN];
                 uint2 sa[RM], sb[RN];
@@ -939,8 +980,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         const uint32_t r2 = fma_abs_rz(av[i].z, bv[j].z, C, tok);
                         const uint32_t r3 = fma_abs_rz(av[i].w, bv[j].w, C, tok);
                         int a = acc[i][j];
-                        a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), (sa[i].x ^ sb[j].x) | 0x00010001u, a);
-                        a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), (sa[i].y ^ sb[j].y) | 0x00010001u, a);
+                        a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), sign_pair(sa[i].x, sb[j].x), a);
+                        a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), sign_pair(sa[i].y, sb[j].y), a);
                         acc[i][j] = a;
                     }
             }
@@ -950,9 +991,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                 for (int i = 0; i < RM; ++i)
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
-                        int a = acc[i][j];
-                        a += (int)quad_xor1((uint32_t)a);
-                        if (G == 4) a += (int)quad_xor2((uint32_t)a);
+                        int a = quad_add<0xB1>(acc[i][j]);
+                        if (G == 4) a = quad_add<0x4E>(a);
                         acc[i][j] = a;
                     }
             }
