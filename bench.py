@@ -9,20 +9,20 @@ Metric: emulated GEMM-ops/s = 2*M*N*K / t, and the fraction of the
 integer-VALU ceiling.
 
 roofline.peak (bound "alu") is the VALU issue ceiling of the path's term
-loop, from the chip's unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes x
-2.4 GHz = 3.93e13 VALU lane-slots/s, divided by the 2.5 lane-slots every
-multiply-add needs in the term loop (one truncating FMA per product; one
-byte permute, one sign-pair bitop and one 16-bit dot product per pair of
-products), times 2 ops per multiply-add: 31.46e12 GEMM-ops/s.  Everything
-else the kernel issues (decode, block maxima, per-block prologue and
-epilogue, addressing) is counted against it.  roofline.frac_vs_R is the
-achieved rate over the survey's op-count model R, which charges 7 packed
-16-bit integer operations per multiply-add (exponent add, block maximum,
-alignment distance, significand product, shift-truncate, sign, accumulate):
-256 x 64 x 2.4e9 x 2 / 7 x 2 = 22.47e12 GEMM-ops/s; the kernel fuses several
-of those into one instruction, so it can exceed R.  roofline.issue_peak is
-the same term loop priced at its instructions' measured issue rates
-(profiles/issue_ceiling.json, from the microbenchmark), when present.
+loop: every multiply-add needs one truncating FMA, and half of a byte
+permute, a sign-pair bitop and a 16-bit dot product (2.5 instructions per
+lane), and that mix issues at 3.38 cycles per wave instruction on gfx950
+(measured, profiles/issue_ceiling.md), so the chip's 1,024 SIMDs at 2.4 GHz
+issue at most 1,024 x 2.4e9 / 3.38 x 64 / 2.5 multiply-adds per second:
+37.23e12 GEMM-ops/s.  Everything else the kernel issues (decode, block
+maxima, per-block prologue and epilogue, addressing) counts against it.
+roofline.issue_peak prices the kernel's own instructions (3.24 lane slots per
+multiply-add, counted in its assembly) at that rate: 28.74e12 GEMM-ops/s.
+roofline.frac_vs_R is the achieved rate over the survey's op-count model R,
+which charges 7 packed 16-bit integer operations per multiply-add (exponent
+add, block maximum, alignment distance, significand product, shift-truncate,
+sign, accumulate): 256 x 64 x 2.4e9 x 2 / 7 x 2 = 22.47e12 GEMM-ops/s; the
+kernel fuses several of those into one instruction, so it can exceed R.
 
 cpu_baseline: the CPU oracle, untuned, timed on the host on a bounded sample
 of the same workload (whole rows of the output), and checked bit for bit
@@ -48,9 +48,10 @@ from bit_exact_fp8_amd import api  # noqa: E402
 from bit_exact_fp8_amd.inputs import (FP8_DTYPES, OUT_DTYPES, WORKLOADS, make_operands,  # noqa: E402
                                       scale_bits)
 
-VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9     # VALU lane-slots/s: CUs x SIMDs x lanes per clock x clock
+SIMDS, CLOCK = 256 * 4, 2.4e9
+TERM_MIX_CYCLES = 3.38                     # cycles per wave instruction of the term mix (measured)
 TERM_LOOP_SLOTS_PER_MAC = 2.5              # fma + (perm + bitop3 + dot2c) / 2
-PEAK_ALU = VALU_LANE_SLOTS / TERM_LOOP_SLOTS_PER_MAC * 2   # GEMM-ops/s
+PEAK_ALU = SIMDS * CLOCK / TERM_MIX_CYCLES * 64 / TERM_LOOP_SLOTS_PER_MAC * 2   # GEMM-ops/s
 R_MODEL = 256 * 64 * 2.4e9 * 2 / 7 * 2    # the survey's op-count model: 7 packed ops per MAC
 METRIC = "bit-exact emulated FP8 GEMM ops/s (2MNK/s) and % of int-VALU roofline"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -388,8 +389,8 @@ def main():
             "peak": PEAK_ALU / 1e12,
             "unit": "T GEMM-ops/s",
             "frac": achieved / PEAK_ALU,
-            "peak_basis": "VALU issue ceiling of the term loop: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz / "
-                          "2.5 lane-slots per multiply-add x 2",
+            "peak_basis": "term-loop issue ceiling: 1024 SIMDs x 2.4 GHz / 3.38 cycles per wave instruction "
+                          "(measured mix) x 64 lanes / 2.5 instructions per multiply-add x 2",
             "traffic": traffic,
             "R": R_MODEL / 1e12,
             "frac_vs_R": achieved / R_MODEL,
@@ -399,7 +400,9 @@ def main():
         },
     }
     ceiling = load_issue_ceiling()
-    if ceiling and ceiling.get("gemm_ops_per_s"):
+    if default_call and wl.name == "mixed_8192" and ceiling and ceiling.get("gemm_ops_per_s"):
+        # the kernel's own instruction mix at the term mix's issue rate (the
+        # 8192^3 kernel: counted in its assembly)
         result["roofline"]["issue_peak"] = ceiling["gemm_ops_per_s"] / 1e12
         result["roofline"]["issue_frac"] = achieved / ceiling["gemm_ops_per_s"]
     if not args.no_cpu_baseline:

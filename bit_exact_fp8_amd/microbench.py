@@ -1,5 +1,5 @@
-"""Issue rates of the main kernel's VALU instruction mix on one MI355X, and
-the sustained shader clock: the measured side of the integer-VALU roofline.
+"""Issue rates of the main kernel's VALU instructions on one MI355X, and of
+its term loop's mix: the measured side of the integer-VALU ceiling.
 
     python -m bit_exact_fp8_amd.microbench [--iters N]
 
@@ -36,17 +36,29 @@ def load():
 
 
 def measure(iters: int = 20000):
+    """One row per instruction (op kernels) and one for the term mix (the
+    last op): wave instructions and lane operations per second over the
+    chip, the rate as a fraction of 16 lanes per SIMD per clock at 2.4 GHz,
+    and, for the term mix, the multiply-add and GEMM-op rates it stands for
+    (5 instructions per 2 multiply-adds)."""
     lib = load()
     rows = []
-    for op in range(lib.mb_op_count()):
+    n = lib.mb_op_count()
+    for op in range(n + 1):
         ms = ctypes.c_double()
         rc = lib.mb_issue_rate(op, iters, BLOCKS, ms)
         if rc != 0:
             raise RuntimeError(f"microbenchmark {op} failed with HIP error {rc}")
-        wave_instr = BLOCKS * 4 * PER_ITER * iters
-        lane_ops = wave_instr * 64 / (ms.value * 1e-3)
-        rows.append({"instruction": lib.mb_op_name(op).decode(), "ms": ms.value,
-                     "lane_ops_per_s": lane_ops, "of_spec_16_lanes_2.4GHz": lane_ops / SPEC_LANE_OPS})
+        per_iter = PER_ITER if op < n else 4 * 8 * 5
+        wave_instr = BLOCKS * 4 * per_iter * iters
+        rate = wave_instr / (ms.value * 1e-3)
+        row = {"instruction": lib.mb_op_name(op).decode(), "ms": ms.value, "instructions_per_s": rate,
+               "lane_ops_per_s": rate * 64, "of_spec_16_lanes_2.4GHz": rate * 64 / SPEC_LANE_OPS,
+               "cycles_per_wave_instruction": SIMDS * 2.4e9 / rate}
+        if op == n:
+            macs = rate * 64 * 2 / 5
+            row.update({"term_mix_macs_per_s": macs, "term_mix_gemm_ops_per_s": 2 * macs})
+        rows.append(row)
     return rows
 
 
