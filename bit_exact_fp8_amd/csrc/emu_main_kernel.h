@@ -74,7 +74,14 @@ constexpr int P_STRIDE = KP + 4; // words per LDS row of the exponent planes
 // (0.151 against 0.155 ms) and 32-product blocks with this one (0.130 against
 // 0.132 ms).
 template <int G, int BLK>
-constexpr int sign_stride() { return (G == 1 || BLK == 32) ? KP + 2 : P_STRIDE; }
+constexpr int sign_stride() { return (G == 4 && BLK == 32) ? KP : (G == 1 || BLK == 32) ? KP + 2 : P_STRIDE; }
+// Words per LDS row of the exponent planes.  With 4 lanes per chain and
+// 32-product blocks, the 8 lanes a 16-byte LDS read serves at a time are 2
+// rows x 4 slices of 16 bytes: rows 64 bytes apart put them on all 32 banks
+// once (the same holds for the sign planes above, read 16 bytes at a time
+// there).
+template <int G, int BLK>
+constexpr int exp_stride() { return (G == 4 && BLK == 32) ? KP : P_STRIDE; }
 
 // Exponent planes (one u16 per code).  A nonzero code stores
 // ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
@@ -662,7 +669,10 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr bool CIN = ACC == ACC_FAST_CIN;
     constexpr bool FAST = ACC == ACC_FAST || CIN, CHUNKS = ACC == ACC_SLOW_CHUNKS;
     constexpr bool RANGED = CHUNKS;  // a group of 128-chunks of the split's k-list per workgroup
-    constexpr int XA = BM * A_STRIDE, XP = BM * P_STRIDE, WA = BN * A_STRIDE, WP = BN * P_STRIDE;
+    constexpr int PST = exp_stride<G, BLK>();
+    // sign words read 16 bytes (two steps of 4 products) at a time
+    constexpr bool SIGN16 = G == 4 && BLK == 32;
+    constexpr int XA = BM * A_STRIDE, XP = BM * PST, WA = BN * A_STRIDE, WP = BN * PST;
     constexpr int SST = sign_stride<G, BLK>();
     constexpr int XS = BM * SST, WS = BN * SST;
 
@@ -817,7 +827,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                                                        xp + ((2 * half + 1) * BM + r) * PW_ROW, r);
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
-                                                  xe + r * P_STRIDE + 8 * half, xs + r * SST + 8 * half);
+                                                  xe + r * PST + 8 * half, xs + r * SST + 8 * half);
                 } else {
                     const int rw = r - BM;
                     if (has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) | has_special<WF>(raw[q].z) |
@@ -832,7 +842,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                                                        wp + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
-                                                  we + rw * P_STRIDE + 8 * half, wsg + rw * SST + 8 * half);
+                                                  we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
                 }
             }
         }
@@ -900,10 +910,10 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         uint4 ea[RM], eb[RN];
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
-                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * P_STRIDE + wo);
+                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * PST + wo);
 #pragma unroll
                         for (int j = 0; j < RN; ++j)
-                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * P_STRIDE + wo);
+                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * PST + wo);
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -917,10 +927,10 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                         uint2 ea[RM], eb[RN];
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
-                            ea[i] = *reinterpret_cast<const uint2 *>(xe + (tm + i * TM) * P_STRIDE + wo);
+                            ea[i] = *reinterpret_cast<const uint2 *>(xe + (tm + i * TM) * PST + wo);
 #pragma unroll
                         for (int j = 0; j < RN; ++j)
-                            eb[j] = *reinterpret_cast<const uint2 *>(we + (tn + j * TN) * P_STRIDE + wo);
+                            eb[j] = *reinterpret_cast<const uint2 *>(we + (tn + j * TN) * PST + wo);
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -956,19 +966,31 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
             // unroll the whole block: its LDS reads then take immediate
             // offsets from one address per plane, and the reads of later
             // steps can overlap earlier arithmetic at 1-2 waves per SIMD)
+            uint4 sa4[SIGN16 ? RM : 1], sb4[SIGN16 ? RN : 1];
 #pragma unroll(PASS_UNROLL)
-            for (int k4 = hb * (BLK / 4) + lane_g * K4PL; k4 < hb * (BLK / 4) + (lane_g + 1) * K4PL; ++k4) {
+            for (int u = 0; u < K4PL; ++u) {
+                const int k4 = hb * (BLK / 4) + lane_g * K4PL + u;
                 float4 av[RM], bv[RN];
                 uint2 sa[RM], sb[RN];
 #pragma unroll
                 for (int i = 0; i < RM; ++i) {
                     av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
-                    sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * SST + 2 * k4);
+                    if constexpr (SIGN16) {
+                        if ((u & 1) == 0) sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + 2 * k4);
+                        sa[i] = (u & 1) ? make_uint2(sa4[i].z, sa4[i].w) : make_uint2(sa4[i].x, sa4[i].y);
+                    } else {
+                        sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * SST + 2 * k4);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
-                    sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * SST + 2 * k4);
+                    if constexpr (SIGN16) {
+                        if ((u & 1) == 0) sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + 2 * k4);
+                        sb[j] = (u & 1) ? make_uint2(sb4[j].z, sb4[j].w) : make_uint2(sb4[j].x, sb4[j].y);
+                    } else {
+                        sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * SST + 2 * k4);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < RM; ++i)
