@@ -27,6 +27,8 @@ constexpr int PER_ITER = 4 * CHAINS;  // instructions per loop iteration (op ker
     X(DOT2_I32_I16, "v_dot2_i32_i16", "v_dot2_i32_i16 %[a], %[b], %[b], %[a]")                                            \
     X(DOT2C_I32_I16, "v_dot2c_i32_i16", "v_dot2c_i32_i16 %[a], %[b], %[b]")                                               \
     X(FMA_F32, "v_fma_f32", "v_fma_f32 %[a], |%[b]|, |%[b]|, %[a]")                                                       \
+    X(FMA_MIX_F32, "v_fma_mix_f32", "v_fma_mix_f32 %[a], |%[b]|, |%[b]|, %[a] op_sel_hi:[1,1,0]")                           \
+    X(CVT_SCALEF32_PK_F16_FP8, "v_cvt_scalef32_pk_f16_fp8", "v_cvt_scalef32_pk_f16_fp8 %[a], %[b], %[sel]")                 \
     X(PERM_B32, "v_perm_b32", "v_perm_b32 %[a], %[b], %[a], %[sel]")                                                      \
     X(BITOP3_B32, "v_bitop3_b32", "v_bitop3_b32 %[a], %[a], %[b], %[sel] bitop3:0xbe")                                    \
     X(LSHRREV_B32, "v_lshrrev_b32", "v_lshrrev_b32 %[a], %[b], %[a]")                                                     \
@@ -152,6 +154,44 @@ __global__ __launch_bounds__(256) void term_mix_kernel(uint32_t *sink, int iters
     sink[gid] = x;
 }
 
+// The same mix with both operands of the pair of products as binary16 halves
+// of one register each (v_fma_mix_f32 with the low, then the high halves).
+__global__ __launch_bounds__(256) void term_mix16_kernel(uint32_t *sink, int iters)
+{
+    const uint32_t b = threadIdx.x * 2654435761u + 12345u;
+    const uint32_t C = 0x4B400000u;
+    uint32_t av[CHAINS], bv[CHAINS];
+    uint32_t sa[CHAINS], acc[CHAINS];
+#pragma unroll
+    for (int j = 0; j < CHAINS; ++j) {
+        av[j] = (((b >> j) & 15u) << 10) | (((b >> (j + 8)) & 15u) << 26);
+        bv[j] = (((b >> (j + 4)) & 15u) << 10) | (((b >> (j + 12)) & 15u) << 26);
+        sa[j] = (b & 0x80008000u) ? 0xFFFF0000u : 0x0000FFFFu;
+        acc[j] = j;
+    }
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < CHAINS; ++j) {
+                uint32_t r0, r1, p, s;
+                asm volatile(
+                    "v_fma_mix_f32 %0, |%6|, |%7|, %8 op_sel_hi:[1,1,0]\n\t"
+                    "v_fma_mix_f32 %1, |%6|, |%7|, %8 op_sel:[1,1,0] op_sel_hi:[1,1,0]\n\t"
+                    "v_perm_b32 %2, %1, %0, %9\n\t"
+                    "v_bitop3_b32 %3, %5, %10, %11 bitop3:0xbe\n\t"
+                    "v_dot2c_i32_i16 %4, %2, %3"
+                    : "=&v"(r0), "=&v"(r1), "=&v"(p), "=&v"(s), "+v"(acc[j])
+                    : "v"(sa[j]), "v"(av[j]), "v"(bv[j]), "v"(C), "s"(0x05040100u), "v"(b), "s"(0x00010001u));
+            }
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < CHAINS; ++j) x ^= acc[j];
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    sink[gid] = x;
+}
+
 template <int OP>
 hipError_t launch(uint32_t *sink, int iters, int blocks)
 {
@@ -169,6 +209,9 @@ hipError_t launch_op(int opi, uint32_t *sink, int iters, int blocks)
     case OP_COUNT:
         hipLaunchKernelGGL(term_mix_kernel, dim3(blocks), dim3(256), 0, 0, sink, iters);
         return hipGetLastError();
+    case OP_COUNT + 1:
+        hipLaunchKernelGGL(term_mix16_kernel, dim3(blocks), dim3(256), 0, 0, sink, iters);
+        return hipGetLastError();
     default: return hipErrorInvalidValue;
     }
 }
@@ -178,13 +221,14 @@ hipError_t launch_op(int opi, uint32_t *sink, int iters, int blocks)
 extern "C" {
 
 // Ops 0 .. mb_op_count()-1 are single instructions (32 per loop iteration);
-// op mb_op_count() is the term mix (4 * 8 groups of 5 instructions per loop
-// iteration).
+// ops mb_op_count() and mb_op_count()+1 are the term mix with binary32 and
+// with binary16 operands (4 * 8 groups of 5 instructions per loop iteration).
 __attribute__((visibility("default"))) int mb_op_count(void) { return OP_COUNT; }
 
 __attribute__((visibility("default"))) const char *mb_op_name(int op)
 {
     if (op == OP_COUNT) return "term mix: 2 v_fma_f32 + v_perm_b32 + v_bitop3_b32 + v_dot2c_i32_i16";
+    if (op == OP_COUNT + 1) return "term mix16: 2 v_fma_mix_f32 + v_perm_b32 + v_bitop3_b32 + v_dot2c_i32_i16";
     return (op >= 0 && op < OP_COUNT) ? kNames[op] : "";
 }
 
@@ -193,7 +237,7 @@ __attribute__((visibility("default"))) const char *mb_op_name(int op)
 // milliseconds of the timed launch (HIP events).  Returns 0, or a hipError_t.
 __attribute__((visibility("default"))) int mb_issue_rate(int op, int iters, int blocks, double *ms)
 {
-    if (op < 0 || op > OP_COUNT || iters < 1 || blocks < 1) return (int)hipErrorInvalidValue;
+    if (op < 0 || op > OP_COUNT + 1 || iters < 1 || blocks < 1) return (int)hipErrorInvalidValue;
     const int64_t threads = (int64_t)blocks * 256;
     uint32_t *sink = nullptr;
     hipEvent_t e0 = nullptr, e1 = nullptr;

@@ -36,15 +36,16 @@ def load():
 
 
 def measure(iters: int = 20000):
-    """One row per instruction (op kernels) and one for the term mix (the
-    last op): wave instructions and lane operations per second over the
-    chip, the rate as a fraction of 16 lanes per SIMD per clock at 2.4 GHz,
-    and, for the term mix, the multiply-add and GEMM-op rates it stands for
-    (5 instructions per 2 multiply-adds)."""
+    """One row per instruction (op kernels) and one for each term mix (the
+    last two ops: binary32 and binary16 operands): wave instructions and
+    lane operations per second over the chip, the rate as a fraction of 16
+    lanes per SIMD per clock at 2.4 GHz, and, for the term mixes, the
+    multiply-add and GEMM-op rates they stand for (5 instructions per 2
+    multiply-adds)."""
     lib = load()
     rows = []
     n = lib.mb_op_count()
-    for op in range(n + 1):
+    for op in range(n + 2):
         ms = ctypes.c_double()
         rc = lib.mb_issue_rate(op, iters, BLOCKS, ms)
         if rc != 0:
@@ -55,7 +56,7 @@ def measure(iters: int = 20000):
         row = {"instruction": lib.mb_op_name(op).decode(), "ms": ms.value, "instructions_per_s": rate,
                "lane_ops_per_s": rate * 64, "of_spec_16_lanes_2.4GHz": rate * 64 / SPEC_LANE_OPS,
                "cycles_per_wave_instruction": SIMDS * 2.4e9 / rate}
-        if op == n:
+        if op >= n:
             macs = rate * 64 * 2 / 5
             row.update({"term_mix_macs_per_s": macs, "term_mix_gemm_ops_per_s": 2 * macs})
         rows.append(row)
