@@ -204,14 +204,16 @@ int choose_tile(int64_t M, int64_t N, int S, const emu_plan_options &opt)
             best = c.cfg;
         }
     }
-    // The 32x32 tile staging 4 K-blocks per barrier instead of 2 hides more
-    // load latency, but its 78 KB of LDS leave room for two workgroups per
-    // CU; measured on MI355X it wins while the grid fits in that (64 x 5760 x
-    // 1920, 360 workgroups: 0.167 against 0.173 ms; 256 x 2048 x 4096, 512:
-    // 0.349 against 0.364 ms) and loses beyond (128 x 5760 x 1920, 720:
-    // 0.257 against 0.234 ms).
-    if (best == emu::TILE_32x32 && ((M + 31) / 32) * ((N + 31) / 32) * (int64_t)S <= 2 * 256)
-        best = emu::TILE_32x32_S4;
+    // The 32x32 tile staging 4 K-blocks per barrier with the block maxima on
+    // the matrix cores issues a sixth fewer VALU instructions than the VALU
+    // maxima and hides more load latency than 2 K-blocks per barrier; its 72
+    // KB of LDS leave room for two workgroups per CU.  Measured on MI355X (A/B
+    // in one session) it wins up to 720 workgroups: 64 x 5760 x 1920 (360)
+    // 0.1445 ms against 0.1588 ms for the 4-stage VALU form; 256 x 2048 x 4096
+    // (512) 0.307 against 0.339 ms; 128 x 5760 x 1920 (720) 0.224 against
+    // 0.228 ms for the 2-stage VALU form, which stays the choice beyond.
+    if (best == emu::TILE_32x32 && ((M + 31) / 32) * ((N + 31) / 32) * (int64_t)S <= 3 * 256)
+        best = emu::TILE_32x32_MX_S4;
     return best;
 }
 

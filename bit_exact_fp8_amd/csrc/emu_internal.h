@@ -119,7 +119,8 @@ enum TileConfig : int {
     TILE_16x8_G4 = 8,
     TILE_16x64_MX = 9,
     TILE_32x32_S4 = 10,
-    TILE_COUNT = 11
+    TILE_32x32_MX_S4 = 11,
+    TILE_COUNT = 12
 };
 
 struct TileShape {

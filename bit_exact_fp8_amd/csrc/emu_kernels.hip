@@ -97,6 +97,7 @@ TileShape tile_shape(int cfg)
     case TILE_16x8_G4: return {16, 8, 512};
     case TILE_16x64_MX: return {16, 64, 64};
     case TILE_32x32_S4: return {32, 32, 256};
+    case TILE_32x32_MX_S4: return {32, 32, 256};
     default: return {64, 128, 256};
     }
 }

@@ -105,29 +105,32 @@ constexpr uint32_t C_OFFSET = (10u << 23) | 0x400000u;
 // 2^q with q = E - 13 has exponent field (E + 127) - 13 = C's field - 23.
 constexpr uint32_t POW2Q_FROM_C = (23u << 23) | 0x400000u;
 
-// Exponent maximum on the matrix cores.  x codes become 2^(4*ex + 5), w codes
-// 2^(4*ew + 4), zeros 0 (bf16 "power planes").  For one quarter-block (8
-// consecutive k), sum_k of the products is S = sum of 2^(4*g_k + 9) over
-// the nonzero products: each term is exact in fp32 and
-// 2^(4G+9) <= S <= 8 * 2^(4G+9) = 2^(4G+12) for G = max g_k, so the binary32
-// exponent field of S, 4G + 136 .. 4G + 139, shifted right by 2 is exactly
-// G + 34.  This holds for any accumulation order and any faithful rounding
-// (the largest term is exact, adding nonnegative terms never goes below it
-// and 8 terms cannot reach 2^(4G+13)), so the matrix instruction's own
-// rounding cannot change the result.  A quarter with no nonzero product
-// gives S = 0, i.e. 0 after the shift, below every real product
-// (G >= -20 -> 14).  The biased block maximum is then
-// E + 127 = max over the four quarters of (S >> 25) + 93, compared with c's
-// binary32 exponent field (|c| >= 2^-33 -> 94 or more, c = 0 -> 0).
-constexpr uint32_t X_POW_OFF = 5;
+// Exponent maximum on the matrix cores.  x codes become 2^(4*ex + 4), w codes
+// 2^(4*ew + 4), zeros 0 (bf16 "power planes"), so the product of a nonzero
+// pair is 2^(4*g + 8).  A 16x16x16 bf16 matrix instruction takes one
+// quarter-block (8 consecutive k) twice: its lanes 32-63 read the same 8 codes
+// as lanes 0-31, so it returns S = 2 * sum of 2^(4*g_k + 8) over the quarter's
+// nonzero products, 16 exact binary32 terms.  With G = max g_k the largest
+// term occurs at least twice and no term exceeds it, so
+// 2^(4G+9) <= S <= 16 * 2^(4G+8) = 2^(4G+12), and the binary32 exponent field
+// of S, 4G + 136 .. 4G + 139, shifted right by 2 is exactly G + 34.  Both
+// bounds are representable and every partial sum of nonnegative terms lies
+// between the largest term and S, so any accumulation order and any faithful
+// rounding keep S inside them: the matrix instruction's own rounding cannot
+// change the result.  A quarter with no nonzero product gives S = 0, i.e. 0
+// after the shift, below every real product (G >= -20 -> 14).  The biased
+// block maximum is then E + 127 = max over the quarters of (S >> 25) + 93,
+// compared with c's binary32 exponent field (|c| >= 2^-33 -> 94 or more,
+// c = 0 -> 0).
+constexpr uint32_t X_POW_OFF = 4;
 constexpr uint32_t W_POW_OFF = 4;
 constexpr uint32_t POW_TO_EB = 93;
-constexpr int PW_ROW = 8;  // words per (quarter, row) of a power plane: 8 real + 8 zero bf16
-// The four 8-byte chunks of a power-plane row are stored XOR-swizzled by bits
-// 2-3 of the row: a matrix instruction's 16 lanes read one chunk of 16
-// consecutive rows, which unswizzled would fall on 4 bank pairs (rows 8 words
-// apart) and swizzled cover all 32 banks.
-__device__ __forceinline__ int pw_chunk(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+constexpr int PW_ROW = 4;  // words per (quarter, row) of a power plane: 8 bf16
+// The two 8-byte chunks of a power-plane row are stored swapped for rows 8-15
+// of every 16: the 16 lanes that read one chunk of 16 consecutive rows (rows
+// 16 bytes apart) then cover all 32 banks once instead of every bank pair
+// twice.
+__device__ __forceinline__ int pw_chunk(int row, int chunk) { return chunk ^ ((row >> 3) & 1); }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
@@ -413,7 +416,7 @@ __device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *
         *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2 *>(vs + 2 * q) = make_uint2(sp[2 * q], sp[2 * q + 1]);
-    // the quarter's 8 codes are chunks 0 and 1 of its row (chunks 2 and 3 stay zero)
+    // the quarter's 8 codes fill the two chunks of its row
     *reinterpret_cast<uint2 *>(pq0 + 2 * pw_chunk(row, 0)) = make_uint2(pp[0], pp[1]);
     *reinterpret_cast<uint2 *>(pq0 + 2 * pw_chunk(row, 1)) = make_uint2(pp[2], pp[3]);
     *reinterpret_cast<uint2 *>(pq1 + 2 * pw_chunk(row, 0)) = make_uint2(pp[4], pp[5]);
@@ -622,6 +625,14 @@ template <int RM, int RN>
 struct WavesPerSimd {
     static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16) ? 3 : 4;
 };
+// Most waves per SIMD the compiler may schedule for: 3 for 4x4 thread tiles
+// (their LDS would let 4 workgroups share a CU, and the compiler then cut the
+// 64x64 matrix-core kernel from 154 to 120 VGPRs, 0.5% slower on 8192^3, A/B
+// in one session), otherwise the hardware's 8.
+template <int RM, int RN>
+struct MaxWavesPerSimd {
+    static constexpr int value = (RM * RN == 16) ? 3 : 8;
+};
 
 // G lanes share each output chain (G = 1, 2 or 4): lane g of a chain takes
 // the g-th of G equal slices of every block; the block maximum and the block
@@ -633,22 +644,28 @@ struct WavesPerSimd {
 // order.
 //
 // MX: the block maximum comes from bf16 matrix instructions (see the power
-// planes above) instead of packed VALU maxima.  Needs RM = 4, G = 1 and one
-// wave per 16 rows: the wave's 16 x (16*RN) output tile is RN 16x16
-// matrix-instruction tiles, and lane l owns rows 4*(l/16) + i and columns
-// l%16 + 16*j, the layout of v_mfma_f32_16x16x16_bf16's result.
+// planes above) instead of packed VALU maxima.  Needs G = 1, RM = 4 or 2 and
+// 4 / RM waves per 16-row band: the band's 16 x (16*RN) outputs are RN 16x16
+// matrix-instruction tiles, and lane l owns columns l%16 + 16*j and rows
+// 4*(l/16) + i, the layout of v_mfma_f32_16x16x16_bf16's result.  With RM = 2
+// the band's two waves h = 0, 1 take rows 4*(l/16) + 2h + i (i = 0, 1): wave h
+// reads the x operand's rows XOR 2h, so that its results 0 and 1 are those
+// rows (both waves issue the band's matrix instructions).
 // Accumulation styles (template parameter ACC): one chain per split; slow
 // accumulation with the running binary32 sum in registers; slow
 // accumulation with each 128-chunk's result stored as a partial.
 constexpr int ACC_FAST = 0, ACC_SLOW = 1, ACC_SLOW_CHUNKS = 2, ACC_FAST_CIN = 3;
 
 template <int XF, int WF, int BM, int BN, int RM, int RN, int G, int ACC, bool MX, int BLK, int SS>
-__global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::value)) void main_kernel(MainParams p)
+__global__ __launch_bounds__((BM / RM) * (BN / RN) * G)
+__attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<RM, RN>::value))) void main_kernel(
+    MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
     static_assert(BLK == 32 || BLK == 16, "blocks of 32 or 16 products");
-    static_assert(!MX || (RM == 4 && G == 1 && BN == 16 * RN && (BM / 16) * 64 == (BM / RM) * (BN / RN)),
-                  "matrix-instruction exponents need 16-row waves with 4x RN thread tiles");
+    static_assert(!MX || ((RM == 4 || RM == 2) && G == 1 && BN == 16 * RN &&
+                          (BM / 16) * (4 / RM) * 64 == (BM / RM) * (BN / RN)),
+                  "matrix-instruction exponents need 4 / RM waves per 16-row band and RM x RN thread tiles");
     constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per stage: two per row
     constexpr int CPT = (NCHUNK * SS + NT - 1) / NT;
@@ -659,7 +676,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr int WU = (WPL >= 4) ? 4 : 2; // words per exponent-plane read
     constexpr int K4PL = BLK / 4 / G;      // groups of 4 products per lane and block
     static_assert(WPL % WU == 0 && K4PL >= 1, "block slice per lane");
-    static_assert(SS >= 1 && (!MX || SS == 1), "stages per barrier: matrix-core exponents use one");
+    static_assert(SS >= 1, "stages per barrier");
     // Unroll of the per-block pass loops: whole blocks for thread tiles of
     // at most 4 outputs (immediate LDS offsets), except the two-stage 2x2
     // tile, whose four waves per SIMD would then spill registers (it keeps
@@ -675,6 +692,7 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     constexpr int XA = BM * A_STRIDE, XP = BM * PST, WA = BN * A_STRIDE, WP = BN * PST;
     constexpr int SST = sign_stride<G, BLK>();
     constexpr int XS = BM * SST, WS = BN * SST;
+    constexpr int XPW = 4 * BM * PW_ROW, WPW = 4 * BN * PW_ROW;  // power-plane words per stage
 
     // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
     __shared__ __attribute__((aligned(16))) float xa_all[SS * XA];
@@ -683,8 +701,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     __shared__ __attribute__((aligned(16))) float wa_all[SS * WA];
     __shared__ __attribute__((aligned(16))) uint32_t we_all[MX ? 4 : SS * WP];
     __shared__ __attribute__((aligned(16))) uint32_t wsg_all[SS * WS];
-    __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? 4 * BM * PW_ROW : 4];
-    __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? 4 * BN * PW_ROW : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t xp[MX ? SS * XPW : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t wp[MX ? SS * WPW : 4];
     __shared__ uint32_t flags[BM + BN + CHUNKS];  // per row (and, for stored chunks, their union)
 
     const int t = threadIdx.x;
@@ -692,14 +710,12 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
     const int c_lo = lane_g == 0 ? -1 : 0, c_hi = lane_g == 0 ? 1 : 0;  // see c_block_term_on
     const int tn = slot % TN, tm = slot / TN;
     const int wave = t >> 6, lane = t & 63;
+    // MX: the wave's 16-row band and, for RM = 2, its half of the band's rows
+    constexpr int BAND_WAVES = MX ? 4 / RM : 1;
+    const int band = wave / BAND_WAVES, half_rows = (RM == 2) ? 2 * (wave % BAND_WAVES) : 0;
     // local row of chain i, local column of chain j
-    auto row_of = [&](int i) { return MX ? 16 * wave + 4 * (lane >> 4) + i : tm + i * TM; };
+    auto row_of = [&](int i) { return MX ? 16 * band + 4 * (lane >> 4) + half_rows + i : tm + i * TM; };
     auto col_of = [&](int j) { return MX ? (lane & 15) + 16 * j : tn + j * TN; };
-
-    if (MX) {  // zero the power planes once: the upper 8 bf16 of every quarter row stay zero
-        for (int i = t; i < BM * PW_ROW; i += NT) reinterpret_cast<uint4 *>(xp)[i] = make_uint4(0, 0, 0, 0);
-        for (int i = t; i < BN * PW_ROW; i += NT) reinterpret_cast<uint4 *>(wp)[i] = make_uint4(0, 0, 0, 0);
-    }
     int tile_m, tile_n;
     tile_order(tile_m, tile_n);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
@@ -823,8 +839,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     if (MX)
                         decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
                                                        xs + r * SST + 8 * half,
-                                                       xp + ((2 * half) * BM + r) * PW_ROW,
-                                                       xp + ((2 * half + 1) * BM + r) * PW_ROW, r);
+                                                       xp + st * XPW + ((2 * half) * BM + r) * PW_ROW,
+                                                       xp + st * XPW + ((2 * half + 1) * BM + r) * PW_ROW, r);
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
                                                   xe + r * PST + 8 * half, xs + r * SST + 8 * half);
@@ -838,8 +854,8 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
                     if (MX)
                         decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
                                                        wsg + rw * SST + 8 * half,
-                                                       wp + ((2 * half) * BN + rw) * PW_ROW,
-                                                       wp + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
+                                                       wp + st * WPW + ((2 * half) * BN + rw) * PW_ROW,
+                                                       wp + st * WPW + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
                                                   we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
@@ -877,12 +893,15 @@ __global__ __launch_bounds__((BM / RM) * (BN / RN) * G, (WavesPerSimd<RM, RN>::v
 #pragma unroll
                 for (int qq = 0; qq < QPB; ++qq) {
                     const int qb = hb * QPB + qq;
-                    const s4 a = *reinterpret_cast<const s4 *>(xp + (qb * BM + 16 * wave + (lane & 15)) * PW_ROW +
-                                                               2 * pw_chunk(lane & 15, lane >> 4));
+                    // lanes 32-63 read the quarter again (its k 8-15 repeat k 0-7)
+                    const int arow = (lane & 15) ^ half_rows;
+                    const s4 a = *reinterpret_cast<const s4 *>(xp + st * XPW + (qb * BM + 16 * band + arow) * PW_ROW +
+                                                               2 * pw_chunk(arow, (lane >> 4) & 1));
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
-                        const s4 b = *reinterpret_cast<const s4 *>(wp + (qb * BN + 16 * j + (lane & 15)) * PW_ROW +
-                                                                   2 * pw_chunk(lane & 15, lane >> 4));
+                        const s4 b = *reinterpret_cast<const s4 *>(wp + st * WPW + (qb * BN + 16 * j + (lane & 15)) *
+                                                                                     PW_ROW +
+                                                                   2 * pw_chunk(lane & 15, (lane >> 4) & 1));
                         const f4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
@@ -1197,6 +1216,7 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_16x8_G4: return launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, S, stream);
     case TILE_16x64_MX: return launch_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_32x32_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, S, stream);
+    case TILE_32x32_MX_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1237,6 +1257,7 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream)
     case TILE_16x8_G4: return launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, stream);
     case TILE_16x64_MX: return launch_cin_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_32x32_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, stream);
+    case TILE_32x32_MX_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
