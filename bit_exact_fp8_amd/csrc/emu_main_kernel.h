@@ -623,7 +623,7 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // which cost it 9% on 8192^3 (49.3 against 44.7 ms, A/B in one session).
 template <int RM, int RN>
 struct WavesPerSimd {
-    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16) ? 3 : 4;
+    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16 || RM * RN == 2) ? 3 : 4;
 };
 // Most waves per SIMD the compiler may schedule for: 3 for 4x4 thread tiles
 // (their LDS would let 4 workgroups share a CU, and the compiler then cut the
@@ -649,8 +649,13 @@ struct MaxWavesPerSimd {
 // matrix-instruction tiles, and lane l owns columns l%16 + 16*j and rows
 // 4*(l/16) + i, the layout of v_mfma_f32_16x16x16_bf16's result.  With RM = 2
 // the band's two waves h = 0, 1 take rows 4*(l/16) + 2h + i (i = 0, 1): wave h
-// reads the x operand's rows XOR 2h, so that its results 0 and 1 are those
-// rows (both waves issue the band's matrix instructions).
+// feeds the instruction its own two rows of every four twice (A rows 4q + i
+// are x rows 4q + 2h + (i & 1)), so that its results i and i + 2 are both row
+// 4q + 2h + i and every result register is read (both waves issue the band's
+// matrix instructions).  With results 2 and 3 unread, the compiler reused
+// their registers while the instruction could still write them: measured on
+// MI355X, wrong block maxima for every second row of the 32x16 tile with
+// 16-product blocks.
 // Accumulation styles (template parameter ACC): one chain per split; slow
 // accumulation with the running binary32 sum in registers; slow
 // accumulation with each 128-chunk's result stored as a partial.
@@ -893,8 +898,10 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
                 for (int qq = 0; qq < QPB; ++qq) {
                     const int qb = hb * QPB + qq;
-                    // lanes 32-63 read the quarter again (its k 8-15 repeat k 0-7)
-                    const int arow = (lane & 15) ^ half_rows;
+                    // lanes 32-63 read the quarter again (its k 8-15 repeat k 0-7);
+                    // with RM = 2, rows 4q + i of the instruction's A take the
+                    // wave's rows 4q + half_rows + (i & 1)
+                    const int arow = (RM == 2) ? ((lane & 12) | half_rows | (lane & 1)) : (lane & 15);
                     const s4 a = *reinterpret_cast<const s4 *>(xp + st * XPW + (qb * BM + 16 * band + arow) * PW_ROW +
                                                                2 * pw_chunk(arow, (lane >> 4) & 1));
 #pragma unroll
@@ -904,8 +911,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                                                                    2 * pw_chunk(lane & 15, (lane >> 4) & 1));
                         const f4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                        for (int i = 0; i < RM; ++i)
-                            smax[i][j] = qq ? max(smax[i][j], __float_as_uint(d[i])) : __float_as_uint(d[i]);
+                        for (int i = 0; i < RM; ++i) {
+                            // RM = 2: results i and i + 2 are the same row; reading
+                            // both leaves no result register unread while the
+                            // instruction may still be writing it
+                            const uint32_t v = (RM == 2) ? max(__float_as_uint(d[i]), __float_as_uint(d[i + 2]))
+                                                         : __float_as_uint(d[i]);
+                            smax[i][j] = qq ? max(smax[i][j], v) : v;
+                        }
                     }
                 }
                 // block prologue: C and the truncated incoming accumulator
@@ -1217,6 +1230,7 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_16x64_MX: return launch_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_32x32_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, S, stream);
     case TILE_32x32_MX_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, S, stream);
+    case TILE_32x16_MX_S3: return launch_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 3>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1258,6 +1272,7 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream)
     case TILE_16x64_MX: return launch_cin_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_32x32_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, stream);
     case TILE_32x32_MX_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, stream);
+    case TILE_32x16_MX_S3: return launch_cin_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 3>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -125,7 +125,7 @@ typedef enum {
 /* Tile configurations of the main kernel (output rows x columns per
  * workgroup; results never depend on the configuration). */
 #define EMU_TILE_AUTO (-1)
-#define EMU_TILE_COUNT 12
+#define EMU_TILE_COUNT 13
 
 /*
  * Plan options, for testing and tuning; a NULL pointer means every field at
@@ -136,7 +136,8 @@ typedef enum {
  *          output; 64x64 and 64x128 with the block exponent maxima on the
  *          matrix cores; 16x8 with 4 lanes per output; 16x64 with
  *          matrix-core maxima in one wave; 32x32 staging 4 K-blocks per
- *          barrier, with VALU or (the last one) matrix-core maxima.
+ *          barrier, with VALU or matrix-core maxima; 32x16 with
+ *          matrix-core maxima staging 3 K-blocks per barrier.
  *   defer: the deferred-infinity plan described at emu_workspace_bytes:
  *          -1 automatic (from 2^36 multiply-adds), 0 never, 1 at every size
  *          the plan allows.  Changes emu_workspace_bytes.
