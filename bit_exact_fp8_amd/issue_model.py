@@ -183,20 +183,61 @@ def model(rates: dict | None, kernel: str = DEFAULT_KERNEL, inner_trips: int = 8
     return res
 
 
+TERM_LOOP_SLOTS_PER_MAC = 2.5  # fma + (perm + bitop3 + dot2c) / 2 per multiply-add
+
+
+def ceilings(rates: dict, term_mix_rate: float, kernel: str = DEFAULT_KERNEL, asm: str | None = None) -> dict:
+    """The issue ceilings of a kernel from measured rates: the term loop alone
+    at the term mix's rate (2.5 instructions per multiply-add), the kernel's
+    own instructions per multiply-add at that rate, and the per-class
+    additive estimate (each opcode class at its own measured rate)."""
+    m = model(rates, kernel, asm=asm)
+    cyc = SIMDS * CLOCK / term_mix_rate  # cycles per wave instruction of the term mix
+    term_ceiling = SIMDS * CLOCK / cyc * 64 / TERM_LOOP_SLOTS_PER_MAC * 2
+    own = SIMDS * CLOCK / cyc * 64 / m["valu_lane_slots_per_mac"] * 2
+    return {
+        "term_mix_cycles_per_wave_instruction": cyc,
+        "term_loop_ceiling_gemm_ops_per_s": term_ceiling,
+        "kernel_valu_per_wave_stage": m["valu_per_wave_stage"],
+        "kernel_macs_per_wave_stage": m["macs_per_wave_stage"],
+        "kernel_valu_lane_slots_per_mac": m["valu_lane_slots_per_mac"],
+        "gemm_ops_per_s": own,
+        "additive_per_class_estimate_gemm_ops_per_s": m.get("issue_ceiling_gemm_ops_per_s"),
+        "unmeasured_opcodes": m.get("unmeasured_opcodes", []),
+        "rates_cycles_per_wave_instruction": {k: round(SIMDS * CLOCK / v, 3) for k, v in rates.items()},
+        "valu_by_opcode_per_wave_stage": m["valu_by_opcode"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--rates", help="JSON lines of bit_exact_fp8_amd.microbench (instruction rates)")
     ap.add_argument("--kernel", default=DEFAULT_KERNEL)
+    ap.add_argument("--json", help="write the issue ceilings (needs --rates) to this file")
     args = ap.parse_args()
-    rates = None
+    rates, term_mix = None, None
     if args.rates:
         rates = {}
         for line in open(args.rates):
             line = line.strip()
             if line.startswith("{"):
                 d = json.loads(line)
-                if "instructions_per_s" in d:
+                if "instructions_per_s" not in d:
+                    continue
+                if d["instruction"].startswith("term mix:"):
+                    term_mix = d["instructions_per_s"]
+                elif not d["instruction"].startswith("term mix"):
                     rates[d["instruction"]] = d["instructions_per_s"]
+    if args.json:
+        if not rates or term_mix is None:
+            raise SystemExit("--json needs --rates with the term mix row")
+        out = {"about": "Issue ceilings of the 8192^3 main kernel (64x64 matrix-core tile, e4m3fn x e5m2, "
+                        "32-product blocks): instruction rates from python3 -m bit_exact_fp8_amd.microbench "
+                        "--iters 20000 on one MI355X, instruction counts from this module on the same sources.",
+               **ceilings(rates, term_mix, args.kernel)}
+        with open(args.json, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
     print(json.dumps(model(rates, args.kernel)), flush=True)
 
 
