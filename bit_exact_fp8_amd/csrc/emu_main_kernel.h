@@ -82,6 +82,13 @@ constexpr int sign_stride() { return (G == 4 && BLK == 32) ? KP : (G == 1 || BLK
 // there).
 template <int G, int BLK>
 constexpr int exp_stride() { return (G == 4 && BLK == 32) ? KP : P_STRIDE; }
+// Words per LDS row of a binary16 value plane (the 4-lane tiles).  With
+// 32-product blocks a 16-byte read serves 8 lanes, 2 rows x 4 slices: rows
+// 64 bytes apart put them on all 32 banks once.  With 16-product blocks an
+// 8-byte read serves 16 lanes, 4 rows x 4 slices of one 32-byte half row:
+// rows 96 bytes apart (24 words: 0, 24, 16, 8 mod 32) do.
+template <int BLK>
+constexpr int half_stride() { return (BLK == 32) ? KP : KP + 8; }
 
 // Exponent planes (one u16 per code).  A nonzero code stores
 // ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
@@ -217,6 +224,16 @@ __device__ __forceinline__ int quad_add(int v)
 // The sign pair (+-1, +-1) of two products from the packed 16-bit sign masks
 // of their x and w codes (0xFFFF negative, 0 positive): (sa ^ sb) | 1 per
 // half, one v_bitop3_b32 (truth table 0xBE: (a ^ b) | c).
+// K4PL steps of 4 binary16 values (2 words each) from LDS: one 16-byte or
+// 8-byte read.
+template <int K4PL>
+__device__ __forceinline__ uint4 load_half_slice(const uint32_t *p)
+{
+    if constexpr (K4PL == 2) return *reinterpret_cast<const uint4 *>(p);
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    return make_uint4(v.x, v.y, 0u, 0u);
+}
+
 __device__ __forceinline__ uint32_t sign_pair(uint32_t sa, uint32_t sb)
 {
     return __builtin_amdgcn_bitop3_b32(sa, sb, 0x00010001u, 0xBE);
@@ -265,6 +282,24 @@ __device__ __forceinline__ uint32_t fma_abs_rz(float a, float b, uint32_t c, uin
 {
     uint32_t r;
     asm("v_fma_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "s"(tok));
+    return r;
+}
+
+// The same with a and b the low (LO) or high (HI) binary16 halves of two
+// registers: v_fma_mix_f32 widens them exactly and forms the same fused
+// product and sum (FP8 values are exact in binary16, subnormals included).
+__device__ __forceinline__ uint32_t fma_abs_rz_lo16(uint32_t a, uint32_t b, uint32_t c, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_fma_mix_f32 %0, |%1|, |%2|, %3 op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b), "v"(c), "s"(tok));
+    return r;
+}
+__device__ __forceinline__ uint32_t fma_abs_rz_hi16(uint32_t a, uint32_t b, uint32_t c, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_fma_mix_f32 %0, |%1|, |%2|, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+        : "=v"(r)
+        : "v"(a), "v"(b), "v"(c), "s"(tok));
     return r;
 }
 
@@ -358,6 +393,15 @@ __device__ __forceinline__ void cvt4(uint32_t w, float &v0, float &v1, float &v2
     }
 }
 
+// Two codes (bytes 0-1, or 2-3 with HI) of a word as two binary16 values
+// (exact hardware conversions, subnormals included), code 0 in the low half.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt2_h(uint32_t w)
+{
+    if (FMT == FMT_E4M3) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8((int)w, 1.0f, HI));
+}
+
 // Exponent-plane pair of two codes held as [code0, 0, code1, 0].
 template <int FMT, uint32_t EBIAS>
 __device__ __forceinline__ uint32_t plane_pair(uint32_t p)
@@ -446,6 +490,32 @@ __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve,
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<uint4 *>(ve + 4 * q) = make_uint4(ep[4 * q], ep[4 * q + 1], ep[4 * q + 2], ep[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2 *>(vs + 2 * q) = make_uint2(sp[2 * q], sp[2 * q + 1]);
+}
+
+// decode_chunk with a binary16 value plane (8 words for the 16 codes).
+template <int FMT, uint32_t EBIAS>
+__device__ __forceinline__ void decode_chunk_h(uint4 raw, uint32_t *vh, uint32_t *ve, uint32_t *vs)
+{
+    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t h[8], ep[8], sp[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = words[q];
+        h[2 * q] = cvt2_h<FMT, false>(w);
+        h[2 * q + 1] = cvt2_h<FMT, true>(w);
+        ep[2 * q] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
+        ep[2 * q + 1] = plane_pair<FMT, EBIAS>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+        const uint32_t t = w << 8;
+        sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
+        sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
+    }
+    *reinterpret_cast<uint4 *>(vh) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4 *>(vh + 4) = make_uint4(h[4], h[5], h[6], h[7]);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
         *reinterpret_cast<uint4 *>(ve + 4 * q) = make_uint4(ep[4 * q], ep[4 * q + 1], ep[4 * q + 2], ep[4 * q + 3]);
@@ -694,7 +764,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     constexpr int PST = exp_stride<G, BLK>();
     // sign words read 16 bytes (two steps of 4 products) at a time
     constexpr bool SIGN16 = G == 4 && BLK == 32;
-    constexpr int XA = BM * A_STRIDE, XP = BM * PST, WA = BN * A_STRIDE, WP = BN * PST;
+    // The 4-lane tiles, bound by LDS bandwidth rather than by the VALU, keep
+    // their value planes in binary16 (half the bytes; the truncating products
+    // then issue as v_fma_mix_f32, whose term mix is 12% slower to issue).
+    constexpr bool V16 = G == 4;
+    constexpr int AHS = half_stride<BLK>();
+    constexpr int XA = V16 ? BM * AHS : BM * A_STRIDE, XP = BM * PST;
+    constexpr int WA = V16 ? BN * AHS : BN * A_STRIDE, WP = BN * PST;
+    static_assert(!V16 || (K4PL <= 2 && !MX), "binary16 values: 4-lane tiles with VALU maxima");
     constexpr int SST = sign_stride<G, BLK>();
     constexpr int XS = BM * SST, WS = BN * SST;
     constexpr int XPW = 4 * BM * PW_ROW, WPW = 4 * BN * PW_ROW;  // power-plane words per stage
@@ -846,6 +923,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                                                        xs + r * SST + 8 * half,
                                                        xp + st * XPW + ((2 * half) * BM + r) * PW_ROW,
                                                        xp + st * XPW + ((2 * half + 1) * BM + r) * PW_ROW, r);
+                    else if (V16)
+                        decode_chunk_h<XF, X_EBIAS>(raw[q], reinterpret_cast<uint32_t *>(xa) + r * AHS + 8 * half,
+                                                    xe + r * PST + 8 * half, xs + r * SST + 8 * half);
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
                                                   xe + r * PST + 8 * half, xs + r * SST + 8 * half);
@@ -861,6 +941,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                                                        wsg + rw * SST + 8 * half,
                                                        wp + st * WPW + ((2 * half) * BN + rw) * PW_ROW,
                                                        wp + st * WPW + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
+                    else if (V16)
+                        decode_chunk_h<WF, W_EBIAS>(raw[q], reinterpret_cast<uint32_t *>(wa) + rw * AHS + 8 * half,
+                                                    we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
                                                   we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
@@ -1005,14 +1088,26 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
             // offsets from one address per plane, and the reads of later
             // steps can overlap earlier arithmetic at 1-2 waves per SIMD)
             uint4 sa4[SIGN16 ? RM : 1], sb4[SIGN16 ? RN : 1];
+            // binary16 values: the lane's whole slice of the block (K4PL steps
+            // of 4 codes, 2 words each) in one read per row
+            uint4 ah4[V16 ? RM : 1], bh4[V16 ? RN : 1];
+            if constexpr (V16) {
+                const int k40 = hb * (BLK / 4) + lane_g * K4PL;
+                const uint32_t *xh = reinterpret_cast<const uint32_t *>(xa);
+                const uint32_t *wh = reinterpret_cast<const uint32_t *>(wa);
+#pragma unroll
+                for (int i = 0; i < RM; ++i) ah4[i] = load_half_slice<K4PL>(xh + row_of(i) * AHS + 2 * k40);
+#pragma unroll
+                for (int j = 0; j < RN; ++j) bh4[j] = load_half_slice<K4PL>(wh + col_of(j) * AHS + 2 * k40);
+            }
 #pragma unroll(PASS_UNROLL)
             for (int u = 0; u < K4PL; ++u) {
                 const int k4 = hb * (BLK / 4) + lane_g * K4PL + u;
-                float4 av[RM], bv[RN];
+                float4 av[V16 ? 1 : RM], bv[V16 ? 1 : RN];
                 uint2 sa[RM], sb[RN];
 #pragma unroll
                 for (int i = 0; i < RM; ++i) {
-                    av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
+                    if constexpr (!V16) av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0) sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + 2 * k4);
                         sa[i] = (u & 1) ? make_uint2(sa4[i].z, sa4[i].w) : make_uint2(sa4[i].x, sa4[i].y);
@@ -1022,7 +1117,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                 }
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
-                    bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
+                    if constexpr (!V16) bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0) sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + 2 * k4);
                         sb[j] = (u & 1) ? make_uint2(sb4[j].z, sb4[j].w) : make_uint2(sb4[j].x, sb4[j].y);
@@ -1035,10 +1130,21 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
                     for (int j = 0; j < RN; ++j) {
                         const uint32_t C = Cb[i][j];
-                        const uint32_t r0 = fma_abs_rz(av[i].x, bv[j].x, C, tok);
-                        const uint32_t r1 = fma_abs_rz(av[i].y, bv[j].y, C, tok);
-                        const uint32_t r2 = fma_abs_rz(av[i].z, bv[j].z, C, tok);
-                        const uint32_t r3 = fma_abs_rz(av[i].w, bv[j].w, C, tok);
+                        uint32_t r0, r1, r2, r3;
+                        if constexpr (V16) {
+                            // step u's codes 0-1 and 2-3 as low / high halves
+                            const uint32_t x0 = (u & 1) ? ah4[i].z : ah4[i].x, x1 = (u & 1) ? ah4[i].w : ah4[i].y;
+                            const uint32_t y0 = (u & 1) ? bh4[j].z : bh4[j].x, y1 = (u & 1) ? bh4[j].w : bh4[j].y;
+                            r0 = fma_abs_rz_lo16(x0, y0, C, tok);
+                            r1 = fma_abs_rz_hi16(x0, y0, C, tok);
+                            r2 = fma_abs_rz_lo16(x1, y1, C, tok);
+                            r3 = fma_abs_rz_hi16(x1, y1, C, tok);
+                        } else {
+                            r0 = fma_abs_rz(av[i].x, bv[j].x, C, tok);
+                            r1 = fma_abs_rz(av[i].y, bv[j].y, C, tok);
+                            r2 = fma_abs_rz(av[i].z, bv[j].z, C, tok);
+                            r3 = fma_abs_rz(av[i].w, bv[j].w, C, tok);
+                        }
                         int a = acc[i][j];
                         a = dot2_i16(__builtin_amdgcn_perm(r1, r0, 0x05040100u), sign_pair(sa[i].x, sb[j].x), a);
                         a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), sign_pair(sa[i].y, sb[j].y), a);
