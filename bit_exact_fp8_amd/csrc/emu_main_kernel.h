@@ -82,13 +82,16 @@ constexpr int sign_stride() { return (G == 4 && BLK == 32) ? KP : (G == 1 || BLK
 // there).
 template <int G, int BLK>
 constexpr int exp_stride() { return (G == 4 && BLK == 32) ? KP : P_STRIDE; }
-// Words per LDS row of a binary16 value plane (the 4-lane tiles).  With
+// Words per LDS row of a binary16 value plane.  4-lane tiles: with
 // 32-product blocks a 16-byte read serves 8 lanes, 2 rows x 4 slices: rows
-// 64 bytes apart put them on all 32 banks once.  With 16-product blocks an
+// 64 bytes apart put them on all 32 banks once; with 16-product blocks an
 // 8-byte read serves 16 lanes, 4 rows x 4 slices of one 32-byte half row:
-// rows 96 bytes apart (24 words: 0, 24, 16, 8 mod 32) do.
-template <int BLK>
-constexpr int half_stride() { return (BLK == 32) ? KP : KP + 8; }
+// rows 96 bytes apart (24 words: 0, 24, 16, 8 mod 32) do.  One lane per
+// output (matrix-core tiles): 16 lanes read 8 bytes at one k from 16
+// consecutive rows, which an odd number of 8-byte pairs (18 words) spreads
+// over all banks.
+template <int G, int BLK>
+constexpr int half_stride() { return (G == 1) ? KP + 2 : (BLK == 32) ? KP : KP + 8; }
 
 // Exponent planes (one u16 per code).  A nonzero code stores
 // ex + 0x200 + bias, with ex its field exponent (emin for subnormals) and
@@ -438,26 +441,40 @@ __device__ __forceinline__ uint32_t power_pair(uint32_t p)
 
 // Decode 16 consecutive codes of one row into the value and sign planes and
 // the power plane (the two quarter-blocks the 16 codes cover, 8 codes each).
-template <int FMT, uint32_t OFF>
+// H: binary16 values, written as four 8-byte pairs (the rows of such planes
+// are 8-byte aligned).
+template <int FMT, uint32_t OFF, bool H = false>
 __device__ __forceinline__ void decode_chunk_pw(uint4 raw, float *va, uint32_t *vs, uint32_t *pq0, uint32_t *pq1,
                                                 int row)
 {
     const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[16];
+    uint32_t h[8];
     uint32_t pp[8], sp[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t w = words[q];
-        cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        if constexpr (H) {
+            h[2 * q] = cvt2_h<FMT, false>(w);
+            h[2 * q + 1] = cvt2_h<FMT, true>(w);
+        } else {
+            cvt4<FMT>(w, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
         pp[2 * q] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C010C00u));
         pp[2 * q + 1] = power_pair<FMT, OFF>(__builtin_amdgcn_perm(0u, w, 0x0C030C02u));
         const uint32_t t = w << 8;
         sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
         sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
     }
+    if constexpr (H) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(va) + 2 * q) = make_uint2(h[2 * q], h[2 * q + 1]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(va + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2 *>(vs + 2 * q) = make_uint2(sp[2 * q], sp[2 * q + 1]);
     // the quarter's 8 codes fill the two chunks of its row
@@ -767,11 +784,12 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     // The 4-lane tiles, bound by LDS bandwidth rather than by the VALU, keep
     // their value planes in binary16 (half the bytes; the truncating products
     // then issue as v_fma_mix_f32, whose term mix is 12% slower to issue).
-    constexpr bool V16 = G == 4;
-    constexpr int AHS = half_stride<BLK>();
+    constexpr bool V16 = G == 4 || (MX && RM == 2);
+    constexpr int AHS = half_stride<G, BLK>();
+    constexpr bool SLICE16 = V16 && K4PL <= 2;  // a lane's whole slice of a block in one read
     constexpr int XA = V16 ? BM * AHS : BM * A_STRIDE, XP = BM * PST;
     constexpr int WA = V16 ? BN * AHS : BN * A_STRIDE, WP = BN * PST;
-    static_assert(!V16 || (K4PL <= 2 && !MX), "binary16 values: 4-lane tiles with VALU maxima");
+    static_assert(!V16 || (G == 4 && K4PL <= 2 && !MX) || (G == 1 && MX), "binary16 value planes");
     constexpr int SST = sign_stride<G, BLK>();
     constexpr int XS = BM * SST, WS = BN * SST;
     constexpr int XPW = 4 * BM * PW_ROW, WPW = 4 * BN * PW_ROW;  // power-plane words per stage
@@ -919,7 +937,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                     float *xa = xa_all + st * XA;
                     uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XS;
                     if (MX)
-                        decode_chunk_pw<XF, X_POW_OFF>(raw[q], xa + r * A_STRIDE + 16 * half,
+                        decode_chunk_pw<XF, X_POW_OFF, V16>(raw[q],
+                                                            V16 ? reinterpret_cast<float *>(
+                                                                      reinterpret_cast<uint32_t *>(xa) + r * AHS +
+                                                                      8 * half)
+                                                                : xa + r * A_STRIDE + 16 * half,
                                                        xs + r * SST + 8 * half,
                                                        xp + st * XPW + ((2 * half) * BM + r) * PW_ROW,
                                                        xp + st * XPW + ((2 * half + 1) * BM + r) * PW_ROW, r);
@@ -937,7 +959,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                     float *wa = wa_all + st * WA;
                     uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WS;
                     if (MX)
-                        decode_chunk_pw<WF, W_POW_OFF>(raw[q], wa + rw * A_STRIDE + 16 * half,
+                        decode_chunk_pw<WF, W_POW_OFF, V16>(raw[q],
+                                                            V16 ? reinterpret_cast<float *>(
+                                                                      reinterpret_cast<uint32_t *>(wa) + rw * AHS +
+                                                                      8 * half)
+                                                                : wa + rw * A_STRIDE + 16 * half,
                                                        wsg + rw * SST + 8 * half,
                                                        wp + st * WPW + ((2 * half) * BN + rw) * PW_ROW,
                                                        wp + st * WPW + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
@@ -1090,8 +1116,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
             uint4 sa4[SIGN16 ? RM : 1], sb4[SIGN16 ? RN : 1];
             // binary16 values: the lane's whole slice of the block (K4PL steps
             // of 4 codes, 2 words each) in one read per row
-            uint4 ah4[V16 ? RM : 1], bh4[V16 ? RN : 1];
-            if constexpr (V16) {
+            uint4 ah4[SLICE16 ? RM : 1], bh4[SLICE16 ? RN : 1];
+            if constexpr (SLICE16) {
                 const int k40 = hb * (BLK / 4) + lane_g * K4PL;
                 const uint32_t *xh = reinterpret_cast<const uint32_t *>(xa);
                 const uint32_t *wh = reinterpret_cast<const uint32_t *>(wa);
@@ -1104,10 +1130,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
             for (int u = 0; u < K4PL; ++u) {
                 const int k4 = hb * (BLK / 4) + lane_g * K4PL + u;
                 float4 av[V16 ? 1 : RM], bv[V16 ? 1 : RN];
+                uint2 ah2[V16 && !SLICE16 ? RM : 1], bh2[V16 && !SLICE16 ? RN : 1];  // step u's binary16 values
                 uint2 sa[RM], sb[RN];
 #pragma unroll
                 for (int i = 0; i < RM; ++i) {
                     if constexpr (!V16) av[i] = *reinterpret_cast<const float4 *>(xa + row_of(i) * A_STRIDE + 4 * k4);
+                    if constexpr (V16 && !SLICE16)
+                        ah2[i] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint32_t *>(xa) +
+                                                                  row_of(i) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0) sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + 2 * k4);
                         sa[i] = (u & 1) ? make_uint2(sa4[i].z, sa4[i].w) : make_uint2(sa4[i].x, sa4[i].y);
@@ -1118,6 +1148,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     if constexpr (!V16) bv[j] = *reinterpret_cast<const float4 *>(wa + col_of(j) * A_STRIDE + 4 * k4);
+                    if constexpr (V16 && !SLICE16)
+                        bh2[j] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint32_t *>(wa) +
+                                                                  col_of(j) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0) sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + 2 * k4);
                         sb[j] = (u & 1) ? make_uint2(sb4[j].z, sb4[j].w) : make_uint2(sb4[j].x, sb4[j].y);
@@ -1133,8 +1166,18 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         uint32_t r0, r1, r2, r3;
                         if constexpr (V16) {
                             // step u's codes 0-1 and 2-3 as low / high halves
-                            const uint32_t x0 = (u & 1) ? ah4[i].z : ah4[i].x, x1 = (u & 1) ? ah4[i].w : ah4[i].y;
-                            const uint32_t y0 = (u & 1) ? bh4[j].z : bh4[j].x, y1 = (u & 1) ? bh4[j].w : bh4[j].y;
+                            uint32_t x0, x1, y0, y1;
+                            if constexpr (SLICE16) {
+                                x0 = (u & 1) ? ah4[i].z : ah4[i].x;
+                                x1 = (u & 1) ? ah4[i].w : ah4[i].y;
+                                y0 = (u & 1) ? bh4[j].z : bh4[j].x;
+                                y1 = (u & 1) ? bh4[j].w : bh4[j].y;
+                            } else {
+                                x0 = ah2[i].x;
+                                x1 = ah2[i].y;
+                                y0 = bh2[j].x;
+                                y1 = bh2[j].y;
+                            }
                             r0 = fma_abs_rz_lo16(x0, y0, C, tok);
                             r1 = fma_abs_rz_hi16(x0, y0, C, tok);
                             r2 = fma_abs_rz_lo16(x1, y1, C, tok);
