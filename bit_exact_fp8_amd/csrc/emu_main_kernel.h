@@ -224,9 +224,6 @@ __device__ __forceinline__ int quad_add(int v)
     return v + __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
-// The sign pair (+-1, +-1) of two products from the packed 16-bit sign masks
-// of their x and w codes (0xFFFF negative, 0 positive): (sa ^ sb) | 1 per
-// half, one v_bitop3_b32 (truth table 0xBE: (a ^ b) | c).
 // K4PL steps of 4 binary16 values (2 words each) from LDS: one 16-byte or
 // 8-byte read.
 template <int K4PL>
@@ -237,6 +234,9 @@ __device__ __forceinline__ uint4 load_half_slice(const uint32_t *p)
     return make_uint4(v.x, v.y, 0u, 0u);
 }
 
+// The sign pair (+-1, +-1) of two products from the packed 16-bit sign masks
+// of their x and w codes (0xFFFF negative, 0 positive): (sa ^ sb) | 1 per
+// half, one v_bitop3_b32 (truth table 0xBE: (a ^ b) | c).
 __device__ __forceinline__ uint32_t sign_pair(uint32_t sa, uint32_t sb)
 {
     return __builtin_amdgcn_bitop3_b32(sa, sb, 0x00010001u, 0xBE);
