@@ -137,14 +137,20 @@ def test_mixed_8192_sampled(dev, orc):
 
 
 # ---- every code pair ------------------------------------------------------------
-@pytest.mark.parametrize("tile", [None, 6, 7, 9])
+# tiles: automatic; the matrix-core maxima of 4-row thread tiles (6: 64x64,
+# 7: 64x128, 9: 16x64) and of 2-row ones with binary16 values (11: 32x32,
+# 12: 32x16); binary16 values with 4 lanes per output (8: 16x8)
+CODE_PAIR_TILES = [None, 6, 7, 9, 8, 11, 12]
+
+
+@pytest.mark.parametrize("tile", CODE_PAIR_TILES)
 @pytest.mark.parametrize("xfmt,wfmt", [("e4m3fn", "e4m3fn"), ("e4m3fn", "e5m2"), ("e5m2", "e4m3fn")])
 def test_every_code_pair(dev, orc, xfmt, wfmt, tile):
     """All 65,536 code pairs, one nonzero product per output (validation
     page, claims table: every pair of FP8 codes through the epilogue), with
-    the automatic tile (one lane per output, packed-maximum exponents) and the
-    three tiles whose block maxima come from the matrix cores (64x64, 64x128,
-    16x64)."""
+    the automatic tile (one lane per output, packed-maximum exponents), the
+    tiles whose block maxima come from the matrix cores, and the tiles that
+    keep binary16 values (truncating with the mixed-precision FMA)."""
     K = 16
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     x = torch.zeros((256, K), dtype=torch.uint8)
@@ -196,7 +202,7 @@ def _adversarial_rows(rows, K, fmt, rng):
     return torch.from_numpy(out)
 
 
-@pytest.mark.parametrize("tile", [None, 6, 7, 9])
+@pytest.mark.parametrize("tile", [None, 6, 7, 9, 11, 12])
 @pytest.mark.parametrize("xfmt,wfmt", [("e4m3fn", "e5m2"), ("e5m2", "e4m3fn"), ("e4m3fn", "e4m3fn")])
 def test_matrix_core_maximum_adversarial(dev, orc, xfmt, wfmt, tile):
     """Blocks built to hit the edges of the matrix-core block maximum: eight
@@ -236,7 +242,7 @@ def test_matrix_core_maximum_extreme_blocks(dev, orc):
     x |= (rng.integers(0, 2, (M, K)) << 7).astype(np.uint8)
     w |= (rng.integers(0, 2, (N, K)) << 7).astype(np.uint8)
     x, w = torch.from_numpy(x), torch.from_numpy(w)
-    for tile in (None, 6, 7, 9):
+    for tile in (None, 6, 7, 9, 11, 12):
         for fast in (True, False):
             check(dev, orc, x, "e4m3fn", w, "e5m2", 1.0, 1.0, "fp32", fast, 1,
                   f"extreme blocks tile {tile} fast={fast}", tile=tile)
