@@ -87,7 +87,7 @@ def abi_version() -> int:
 
 
 TILE_CONFIGS = ("64x128", "64x64", "32x64", "32x32", "16x16_g2", "16x16_g4", "64x64_mx", "64x128_mx",
-                "16x8_g4", "16x64_mx", "32x32_s4", "32x32_mx_s4", "32x16_mx_s3")
+                "16x8_g4", "16x64_mx", "32x32_s4", "32x32_mx_s4", "32x16_mx_s5")
 DEFER_MODES = {"auto": -1, "off": 0, "on": 1}
 
 

@@ -216,14 +216,16 @@ int choose_tile(int64_t M, int64_t N, int S, const emu_plan_options &opt)
     // 0.315 and 0.232 ms on the last two.)
     // Between 257 and 384 such workgroups, the CUs that hold two of them set
     // the time while the others idle for half of it; the 32x16 form of the
-    // same tile (2x1 thread tiles, 3 K-blocks per barrier, three workgroups
+    // same tile (2x1 thread tiles, 5 K-blocks per barrier, three workgroups
     // per CU) splits the work finer: 64 x 5760 x 1920 (360 32x32 workgroups)
-    // 0.136 against 0.144 ms.  With whole rounds of 32x32 workgroups it only
-    // costs (256 x 2048 x 4096, 512: 0.378 against 0.305 ms).
+    // 0.130 against 0.144 ms (with 2, 3 and 4 K-blocks per barrier 0.136,
+    // 0.134 and 0.132 ms; 6 would leave room for two workgroups per CU only).
+    // With whole rounds of 32x32 workgroups it only costs (256 x 2048 x 4096,
+    // 512: 0.378 against 0.305 ms with 3 K-blocks per barrier).
     if (best == emu::TILE_32x32) {
         const int64_t wgs = ((M + 31) / 32) * ((N + 31) / 32) * (int64_t)S;
         if (wgs > 256 && wgs <= 384)
-            best = emu::TILE_32x16_MX_S3;
+            best = emu::TILE_32x16_MX_S5;
         else if (wgs <= 3 * 256)
             best = emu::TILE_32x32_MX_S4;
     }

@@ -120,7 +120,7 @@ enum TileConfig : int {
     TILE_16x64_MX = 9,
     TILE_32x32_S4 = 10,
     TILE_32x32_MX_S4 = 11,
-    TILE_32x16_MX_S3 = 12,
+    TILE_32x16_MX_S5 = 12,
     TILE_COUNT = 13
 };
 

@@ -98,7 +98,7 @@ TileShape tile_shape(int cfg)
     case TILE_16x64_MX: return {16, 64, 64};
     case TILE_32x32_S4: return {32, 32, 256};
     case TILE_32x32_MX_S4: return {32, 32, 256};
-    case TILE_32x16_MX_S3: return {32, 16, 256};
+    case TILE_32x16_MX_S5: return {32, 16, 256};
     default: return {64, 128, 256};
     }
 }

@@ -1379,7 +1379,7 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_16x64_MX: return launch_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_32x32_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, S, stream);
     case TILE_32x32_MX_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, S, stream);
-    case TILE_32x16_MX_S3: return launch_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 3>(p, S, stream);
+    case TILE_32x16_MX_S5: return launch_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 5>(p, S, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1421,7 +1421,7 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream)
     case TILE_16x64_MX: return launch_cin_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_32x32_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, stream);
     case TILE_32x32_MX_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, stream);
-    case TILE_32x16_MX_S3: return launch_cin_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 3>(p, stream);
+    case TILE_32x16_MX_S5: return launch_cin_cfg<XF, WF, 32, 16, 2, 1, 1, true, BLK, 5>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -137,7 +137,7 @@ typedef enum {
  *          matrix cores; 16x8 with 4 lanes per output; 16x64 with
  *          matrix-core maxima in one wave; 32x32 staging 4 K-blocks per
  *          barrier, with VALU or matrix-core maxima; 32x16 with
- *          matrix-core maxima staging 3 K-blocks per barrier.
+ *          matrix-core maxima staging 5 K-blocks per barrier.
  *   defer: the deferred-infinity plan described at emu_workspace_bytes:
  *          -1 automatic (from 2^36 multiply-adds), 0 never, 1 at every size
  *          the plan allows.  Changes emu_workspace_bytes.
