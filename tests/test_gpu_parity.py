@@ -328,6 +328,27 @@ def test_stage_forms_of_the_32x32_tile(dev, orc, shape, forced):
               f"32x32 stage forms {shape} tile {forced}", tile=forced)
 
 
+@pytest.mark.parametrize("profile", ["hopper", "ada-pairwise"])
+def test_16x8_tile_long_klists(dev, orc, profile):
+    """The 16x8 tile with 4 lanes per output stages 16 K-blocks per barrier
+    on long k-lists (8 on short ones): a ragged K whose last round is
+    partial (2960 = 92.5 stages of 32), fast and slow, unsplit and split
+    into k-lists of different lengths, NaN / Inf codes in one row, and chains
+    from incoming accumulators, against the oracle."""
+    M, N, K = 17, 48, 2960
+    gen = torch.Generator().manual_seed(2960)
+    x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
+    w = inject(random_codes((N, K), "e5m2", gen), "e5m2", 0.1, 0.05, gen)
+    w[5, 1999] = 0x7C  # an infinity in one column
+    for fast, S in ((True, 1), (False, 1), (True, 3), (False, 2), (True, 2)):
+        check(dev, orc, x, "e4m3fn", w, "e5m2", 0.1, 1 / 3, "bf16", fast, S,
+              f"16x8 tile, long k-list, {profile}", profile=profile, tile=8)
+    c = _c_patterns(M, N, np.random.default_rng(7))
+    got = gpu_accumulate_c(dev, x, "e4m3fn", w, "e5m2", c, profile, tile=8)
+    want = orc.accumulate_c(x.numpy(), "e4m3fn", w.numpy(), "e5m2", c, profile=profile)
+    assert_same(got, want, f"16x8 tile, long k-list, incoming accumulators, {profile}")
+
+
 @pytest.mark.parametrize("seed", [101, 102])
 def test_randomized_cases(dev, orc, seed):
     """200 seeded random problems per seed: ragged shapes (K = 0 included),
