@@ -311,35 +311,52 @@ __device__ __forceinline__ uint32_t fma_abs_rz_hi16(uint32_t a, uint32_t b, uint
 // the result, below 2^15), times c's sign: the sign from c's bits read as a
 // signed integer, clamped to [-1, 1] (-0 gives -1, which only multiplies a
 // zero magnitude), and a signed 16-bit multiply, in one statement so that no
-// wait is placed between its three dependent instructions.  (A form with the
-// sign as the 16-bit pair (+-1, 0) and a dot product takes one instruction
-// more; on MI355X it measured slower in every kernel once the LDS planes were
-// free of bank conflicts: 8192^3 hopper 43.4 against 42.3 ms.)
-__device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t tok)
+// wait is placed between its three dependent instructions; `base` is added
+// (the block sum's offset, see kSumBase).  (A form with the sign as the
+// 16-bit pair (+-1, 0) and a dot product takes one instruction more; on
+// MI355X it measured slower in every kernel once the LDS planes were free of
+// bank conflicts: 8192^3 hopper 43.4 against 42.3 ms.)
+__device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t tok, uint32_t base)
 {
     int acc;
     uint32_t sgn, r;
     asm("v_med3_i32 %1, %3, -1, 1\n\t"
         "v_fma_f32 %2, |%3|, 1.0, %4\n\t"
-        "v_mad_i32_i16 %0, %2, %1, 0"
+        "v_mad_i32_i16 %0, %2, %1, %6"
         : "=v"(acc), "=&v"(sgn), "=&v"(r)
-        : "v"(c), "v"(Cb), "s"(tok));
+        : "v"(c), "v"(Cb), "s"(tok), "s"(base));
     return acc;
 }
 
 // The same term where G lanes share a chain and it enters the block sum on
 // one lane only: that lane clamps c's bits to [lo, hi] = [-1, 1], the others
-// to [0, 0], so their term is 0 without a separate select.
-__device__ __forceinline__ int c_block_term_on(uint32_t c, uint32_t Cb, uint32_t tok, int lo, int hi)
+// to [0, 0], so their term is 0 without a separate select; `base` is that
+// lane's offset (0 on the others).
+__device__ __forceinline__ int c_block_term_on(uint32_t c, uint32_t Cb, uint32_t tok, int lo, int hi, uint32_t base)
 {
     int acc;
     uint32_t sgn, r;
     asm("v_med3_i32 %1, %3, %6, %7\n\t"
         "v_fma_f32 %2, |%3|, 1.0, %4\n\t"
-        "v_mad_i32_i16 %0, %2, %1, 0"
+        "v_mad_i32_i16 %0, %2, %1, %8"
         : "=v"(acc), "=&v"(sgn), "=&v"(r)
-        : "v"(c), "v"(Cb), "s"(tok), "v"(lo), "v"(hi));
+        : "v"(c), "v"(Cb), "s"(tok), "v"(lo), "v"(hi), "v"(base));
     return acc;
+}
+
+// The block sum n (|n| < 2^21: at most 32 terms and c's, each below 2^15)
+// accumulates from kSumBase, the bits of 1.5 * 2^23, so that its bits read as
+// a binary32 are exactly 1.5 * 2^23 + n.  Then, with Cb = 1.5 * 2^(E+10) =
+// 1.5 * 2^23 * 2^q and 2^q the block's quantum, fma(1.5 * 2^23 + n, 2^q, -Cb)
+// is n * 2^q exactly (at most 21 significant bits): the conversion and the
+// scaling in one instruction.
+constexpr uint32_t kSumBase = 0x4B400000u;
+
+__device__ __forceinline__ uint32_t scale_block_sum(uint32_t sum_bits, uint32_t q, uint32_t Cb, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_fma_f32 %0, %1, %2, -%3" : "=v"(r) : "v"(sum_bits), "v"(q), "v"(Cb), "s"(tok));
+    return r;
 }
 
 // a * b where the product is exact (a power of two times a value of at most
@@ -866,17 +883,66 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
         for (int q = 0; q < CPT; ++q) chunk_row[q] = chunk_row_of(q);
     }
-    auto load_block = [&](int64_t pos) {
+    // Several stages per barrier over a contiguous k-list (position sp is
+    // k = k0 + sp): chunk q of this thread, at offset off = stage * 32 + half
+    // from the barrier's first position pos, reads chunk_base[q] + k0 + pos
+    // (its row pointer with the offset folded in) while off is below both the
+    // k-list's end and K, measured from pos; chunks without a row get an
+    // offset no bound reaches.
+    constexpr bool MULTI = SS > 1 && KEEP_ROWS;
+    const uint8_t *chunk_base[MULTI ? CPT : 1];
+    int chunk_off[MULTI ? CPT : 1];
+    if constexpr (MULTI) {
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
-            const int half = 16 * (idx & 1);
-            raw[q] = make_uint4(0, 0, 0, 0);
-            const int64_t sp = pos + (int64_t)(idx / NCHUNK) * KB;
-            const uint8_t *row = KEEP_ROWS ? chunk_row[KEEP_ROWS ? q : 0] : chunk_row_of(q);
-            if (row && sp < pos_end) {
-                const int64_t k = sq.k_of(sp);
-                if (k + half < p.K) raw[q] = *reinterpret_cast<const uint4 *>(row + k);
+            const int stk = (idx / NCHUNK) * KB;
+            chunk_base[q] = chunk_row[q] ? chunk_row[q] + stk : p.x;
+            chunk_off[q] = chunk_row[q] ? stk + 16 * (idx & 1) : INT32_MAX;
+        }
+    }
+    auto load_block = [&](int64_t pos) {
+        if constexpr (SS == 1) {
+            // one stage per barrier: every chunk sits at position pos (inside
+            // the k-list: the callers check), whose k is the same for the
+            // whole workgroup and is formed by scalar instructions.  (Reading
+            // chunks without codes from a zero constant instead of zeroing
+            // them made these loads flat ones, which also count as LDS
+            // accesses: 8192^3 41.2 against 40.2 ms.)
+            const int64_t k = sq.k_of(pos);
+#pragma unroll
+            for (int q = 0; q < CPT; ++q) {
+                const int half = 16 * ((t + q * NT) & 1);
+                const uint8_t *row = KEEP_ROWS ? chunk_row[KEEP_ROWS ? q : 0] : chunk_row_of(q);
+                raw[q] = make_uint4(0, 0, 0, 0);
+                if (row && k + half < p.K) raw[q] = *reinterpret_cast<const uint4 *>(row + k);
+            }
+        } else {
+            if (MULTI && !p.round_robin) {
+                // the contiguous k-list (uniform branch): one scalar bound
+                const int64_t kp = (sq.first << sq.shift) + pos;
+                int64_t lim = pos_end - pos;
+                if (p.K - kp < lim) lim = p.K - kp;
+                const int lim32 = (int)(lim < KB * SS ? lim : KB * SS);
+#pragma unroll
+                for (int q = 0; q < CPT; ++q) {
+                    raw[q] = make_uint4(0, 0, 0, 0);
+                    if (chunk_off[MULTI ? q : 0] < lim32)
+                        raw[q] = *reinterpret_cast<const uint4 *>(chunk_base[MULTI ? q : 0] + kp);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < CPT; ++q) {
+                    const int idx = t + q * NT;
+                    const int half = 16 * (idx & 1);
+                    raw[q] = make_uint4(0, 0, 0, 0);
+                    const int64_t sp = pos + (int64_t)(idx / NCHUNK) * KB;
+                    const uint8_t *row = KEEP_ROWS ? chunk_row[KEEP_ROWS ? q : 0] : chunk_row_of(q);
+                    if (row && sp < pos_end) {
+                        const int64_t k = sq.k_of(sp);
+                        if (k + half < p.K) raw[q] = *reinterpret_cast<const uint4 *>(row + k);
+                    }
+                }
             }
         }
     };
@@ -894,6 +960,10 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     // Incoming accumulators keep c cut after every block (they select c
     // itself on some blocks).
     constexpr bool CUT_EACH_BLOCK = CIN;
+    // the block sums' offset (kSumBase where the epilogue reads it), entered
+    // once per chain: with the incoming c's term, on the chain's first lane
+    constexpr uint32_t SUM_BASE = CUT_EACH_BLOCK ? 0u : kSumBase;
+    const uint32_t base_on = lane_g == 0 ? SUM_BASE : 0u;
     uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -1041,7 +1111,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         // the hopper incoming-accumulator kernel: left out there)
                         if constexpr (!(CIN && BLK == 32)) asm("" : "+v"(cb));
                         Cb[i][j] = cb;
-                        acc[i][j] = c_block_term(c[i][j], Cb[i][j], tok);
+                        acc[i][j] = c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             } else {
@@ -1103,8 +1173,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         asm("" : "+v"(cb));  // later uses derive from C itself
                         Cb[i][j] = cb;
                         // c enters the block sum once
-                        acc[i][j] = (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok)
-                                             : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi);
+                        acc[i][j] = (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE)
+                                             : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi, base_on);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             }
@@ -1206,14 +1276,19 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                     }
             }
 
-            // block epilogue: cut the exact sum to 14 significant bits, scale by 2^q
+            // block epilogue: the exact sum scaled by 2^q (cut to 14 significant
+            // bits first where c must stay cut after every block)
 #pragma unroll
             for (int i = 0; i < RM; ++i)
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
-                    const uint32_t tf = __float_as_uint((float)acc[i][j]);
-                    const uint32_t tb = CUT_EACH_BLOCK ? cut14(tf) : tf;
-                    const uint32_t cn = mul_exact(tb, Cb[i][j] - POW2Q_FROM_C, tok);
+                    uint32_t cn;
+                    if constexpr (CUT_EACH_BLOCK) {
+                        const uint32_t tf = __float_as_uint((float)acc[i][j]);
+                        cn = mul_exact(cut14(tf), Cb[i][j] - POW2Q_FROM_C, tok);
+                    } else {
+                        cn = scale_block_sum((uint32_t)acc[i][j], Cb[i][j] - POW2Q_FROM_C, Cb[i][j], tok);
+                    }
                     if constexpr (CIN) {
                         // c (cut to 14 significant bits by the prologue) stays when
                         // the block exponent, biased, is below 94 -- no products
