@@ -579,6 +579,27 @@ __device__ __forceinline__ uint32_t special_flags(uint4 raw)
     return nan ? 3u : 1u;
 }
 
+// A chunk's row flags where `hit` marks special codes in it.  NaN / Inf codes
+// are rare: with BRANCH (tiles whose waves decode only x or only w rows) the
+// flags are formed only where a lane of the wave holds one -- the empty
+// volatile statement keeps that a branch, which the compiler would otherwise
+// turn into forming them for every chunk and selecting (2048 x 5760 x 1920
+// 1.96 -> 1.92 ms, 8192^3 unchanged, A/B in one session); tiles whose waves
+// decode both keep the select (the 32x16 tile measured 4% slower with the
+// branch).
+template <int FMT, bool BRANCH>
+__device__ __forceinline__ void rare_flags(uint32_t &flag, uint32_t hit, uint4 raw)
+{
+    if constexpr (BRANCH) {
+        if (__any(hit != 0)) {
+            asm volatile("");
+            if (hit) flag |= special_flags<FMT>(raw);
+        }
+    } else {
+        if (hit) flag |= special_flags<FMT>(raw);
+    }
+}
+
 // The k-list of one split: positions 0 .. len-1 along its k-tiles (width
 // 2^shift; tile `first`, then every `stride`-th), k = tile * W + offset.
 struct SplitSeq {
@@ -778,6 +799,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per stage: two per row
     constexpr int CPT = (NCHUNK * SS + NT - 1) / NT;
+    // every wave decodes x rows only or w rows only
+    constexpr bool FLAG_BRANCH = (2 * BM) % 64 == 0 && NCHUNK % 64 == 0 && NT % 64 == 0;
     constexpr int NBS = KB / BLK;          // blocks per stage
     constexpr int QPB = BLK / 8;           // quarter-blocks (8 products) per block
     constexpr int WPB = BLK / 2;           // exponent-plane words per block
@@ -1001,9 +1024,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                 const int st = idx / NCHUNK, c = idx % NCHUNK;
                 const int r = c >> 1, half = c & 1;
                 if (r < BM) {
-                    if (has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) | has_special<XF>(raw[q].z) |
-                        has_special<XF>(raw[q].w))
-                        myflag[q] |= special_flags<XF>(raw[q]);  // rare: NaN / Inf codes
+                    const uint32_t hit = has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
+                                         has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
+                    rare_flags<XF, FLAG_BRANCH>(myflag[q], hit, raw[q]);
                     float *xa = xa_all + st * XA;
                     uint32_t *xe = xe_all + (MX ? 0 : st * XP), *xs = xs_all + st * XS;
                     if (MX)
@@ -1023,9 +1046,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                                                   xe + r * PST + 8 * half, xs + r * SST + 8 * half);
                 } else {
                     const int rw = r - BM;
-                    if (has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) | has_special<WF>(raw[q].z) |
-                        has_special<WF>(raw[q].w))
-                        myflag[q] |= special_flags<WF>(raw[q]);  // rare: NaN / Inf codes
+                    const uint32_t hit = has_special<WF>(raw[q].x) | has_special<WF>(raw[q].y) |
+                                         has_special<WF>(raw[q].z) | has_special<WF>(raw[q].w);
+                    rare_flags<WF, FLAG_BRANCH>(myflag[q], hit, raw[q]);
                     float *wa = wa_all + st * WA;
                     uint32_t *we = we_all + (MX ? 0 : st * WP), *wsg = wsg_all + st * WS;
                     if (MX)
