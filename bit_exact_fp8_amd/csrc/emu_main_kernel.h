@@ -586,7 +586,7 @@ __device__ __forceinline__ uint32_t special_flags(uint4 raw)
 // turn into forming them for every chunk and selecting (2048 x 5760 x 1920
 // 1.96 -> 1.92 ms, 8192^3 unchanged, A/B in one session); tiles whose waves
 // decode both keep the select (the 32x16 tile measured 4% slower with the
-// branch).
+// branch while its waves held both).
 template <int FMT, bool BRANCH>
 __device__ __forceinline__ void rare_flags(uint32_t &flag, uint32_t hit, uint4 raw)
 {
@@ -799,8 +799,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     constexpr int TM = BM / RM, TN = BN / RN, NT = TM * TN * G;
     constexpr int NCHUNK = 2 * (BM + BN);  // 16-byte chunks per stage: two per row
     constexpr int CPT = (NCHUNK * SS + NT - 1) / NT;
+    constexpr int NXC = 2 * BM * SS;  // x chunks per barrier round, numbered first
     // every wave decodes x rows only or w rows only
-    constexpr bool FLAG_BRANCH = (2 * BM) % 64 == 0 && NCHUNK % 64 == 0 && NT % 64 == 0;
+    constexpr bool FLAG_BRANCH = NXC % 64 == 0 && NT % 64 == 0;
     constexpr int NBS = KB / BLK;          // blocks per stage
     constexpr int QPB = BLK / 8;           // quarter-blocks (8 products) per block
     constexpr int WPB = BLK / 2;           // exponent-plane words per block
@@ -870,15 +871,18 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 
     for (int i = t; i < BM + BN + CHUNKS; i += NT) flags[i] = 0;
 
-    // chunk q of this thread: row r = idx >> 1 (x rows first), half = idx & 1
     uint32_t myflag[CPT];
     uint4 raw[CPT];
 #pragma unroll
     for (int q = 0; q < CPT; ++q) myflag[q] = 0;
 
     // Stages at sequence positions pos, pos + 32, ..., pos + 32*(SS-1) (each a
-    // multiple of 32 inside one k-tile): chunk idx = t + q*NT is stage
-    // idx / NCHUNK, row (idx % NCHUNK) >> 1 (x rows first), half idx & 1.
+    // multiple of 32 inside one k-tile), 2 16-byte chunks per row and stage:
+    // chunk idx = t + q*NT numbers the x chunks of all SS stages first
+    // (stage idx / (2*BM), row (idx % (2*BM)) >> 1), then the w chunks (row
+    // index BM + that of idx - NXC), half idx & 1.  With NXC a multiple of
+    // 64, every wave decodes x rows only or w rows only (a wave holding both
+    // runs both decode paths, one after the other).
     // A 32-wide stage never straddles a k-tile (tiles are 64 or 128 wide and
     // stages start at multiples of 32 of the k-list), and only the last
     // k-tile of K can be short, so a chunk is loaded when its k is below K;
@@ -888,9 +892,20 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     // whole walk: small thread tiles keep them in registers, large ones
     // (whose register budget is tight) recompute them at every load.
     constexpr bool KEEP_ROWS = RM * RN <= 4;
+    // (one stage per barrier: the same order as idx % NCHUNK, which the
+    // 64x64 kernel keeps -- the general form cost it 1.9% on 8192^3)
+    auto chunk_stage = [&](int idx) {
+        if constexpr (SS == 1) return 0;
+        return idx < NXC ? idx / (2 * BM) : (idx - NXC) / (2 * BN);
+    };
+    auto chunk_rowidx = [&](int idx) {
+        if constexpr (SS == 1) return (idx % NCHUNK) >> 1;
+        return idx < NXC ? (idx % (2 * BM)) >> 1 : BM + (((idx - NXC) % (2 * BN)) >> 1);
+    };
     auto chunk_row_of = [&](int q) -> const uint8_t * {
         const int idx = t + q * NT;
-        const int c = idx % NCHUNK, r = c >> 1;
+        const int c = (SS == 1) ? idx % NCHUNK : idx;  // c: the half's parity
+        const int r = (SS == 1) ? c >> 1 : chunk_rowidx(idx);
         const uint8_t *row = nullptr;
         if (idx < NCHUNK * SS) {
             if (r < BM) {
@@ -919,7 +934,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
-            const int stk = (idx / NCHUNK) * KB;
+            const int stk = chunk_stage(idx) * KB;
             chunk_base[q] = chunk_row[q] ? chunk_row[q] + stk : p.x;
             chunk_off[q] = chunk_row[q] ? stk + 16 * (idx & 1) : INT32_MAX;
         }
@@ -959,7 +974,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                     const int idx = t + q * NT;
                     const int half = 16 * (idx & 1);
                     raw[q] = make_uint4(0, 0, 0, 0);
-                    const int64_t sp = pos + (int64_t)(idx / NCHUNK) * KB;
+                    const int64_t sp = pos + (int64_t)chunk_stage(idx) * KB;
                     const uint8_t *row = KEEP_ROWS ? chunk_row[KEEP_ROWS ? q : 0] : chunk_row_of(q);
                     if (row && sp < pos_end) {
                         const int64_t k = sq.k_of(sp);
@@ -1021,8 +1036,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
         for (int q = 0; q < CPT; ++q) {
             const int idx = t + q * NT;
             if (idx < NCHUNK * SS) {
-                const int st = idx / NCHUNK, c = idx % NCHUNK;
-                const int r = c >> 1, half = c & 1;
+                const int c = (SS == 1) ? idx % NCHUNK : idx;
+                const int st = (SS == 1) ? idx / NCHUNK : chunk_stage(idx);
+                const int r = (SS == 1) ? c >> 1 : chunk_rowidx(idx), half = c & 1;
                 if (r < BM) {
                     const uint32_t hit = has_special<XF>(raw[q].x) | has_special<XF>(raw[q].y) |
                                          has_special<XF>(raw[q].z) | has_special<XF>(raw[q].w);
@@ -1374,7 +1390,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     for (int q = 0; q < CPT; ++q) {
         const int idx = t + q * NT;
         if (idx < NCHUNK * SS && myflag[q]) {
-            atomicOr(&flags[(idx % NCHUNK) >> 1], myflag[q]);
+            atomicOr(&flags[chunk_rowidx(idx)], myflag[q]);
             if (CHUNKS) atomicOr(&flags[BM + BN], myflag[q]);
         }
     }
