@@ -55,6 +55,7 @@ constexpr int PER_ITER = 4 * CHAINS;  // instructions per loop iteration (op ker
     X(PK_MAX_U16, "v_pk_max_u16", "v_pk_max_u16 %[a], %[a], %[b]")                                                        \
     X(PK_MIN_U16, "v_pk_min_u16", "v_pk_min_u16 %[a], %[a], %[b]")                                                        \
     X(PK_MUL_LO_U16, "v_pk_mul_lo_u16", "v_pk_mul_lo_u16 %[a], %[a], %[b]")                                               \
+    X(PK_MAD_U16, "v_pk_mad_u16", "v_pk_mad_u16 %[a], %[a], %[b], %[b]")                                                  \
     X(PK_LSHRREV_B16, "v_pk_lshrrev_b16", "v_pk_lshrrev_b16 %[a], 3, %[a] op_sel_hi:[0,1]")                               \
     X(PK_LSHLREV_B16, "v_pk_lshlrev_b16", "v_pk_lshlrev_b16 %[a], 9, %[a] op_sel_hi:[0,1]")                               \
     X(CVT_PK_F32_FP8, "v_cvt_pk_f32_fp8", "v_cvt_pk_f32_fp8 %[a64], %[b]")                                                \
