@@ -328,6 +328,20 @@ __device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t to
     return acc;
 }
 
+// The same term with the block sum starting from Cb's own bits (see
+// sub_block_base): Cb is both the truncating addend and the sum's offset.
+__device__ __forceinline__ int c_block_term_cb(uint32_t c, uint32_t Cb, uint32_t tok)
+{
+    int acc;
+    uint32_t sgn, r;
+    asm("v_med3_i32 %1, %3, -1, 1\n\t"
+        "v_fma_f32 %2, |%3|, 1.0, %4\n\t"
+        "v_mad_i32_i16 %0, %2, %1, %4"
+        : "=v"(acc), "=&v"(sgn), "=&v"(r)
+        : "v"(c), "v"(Cb), "s"(tok));
+    return acc;
+}
+
 // The same term where G lanes share a chain and it enters the block sum on
 // one lane only: that lane clamps c's bits to [lo, hi] = [-1, 1], the others
 // to [0, 0], so their term is 0 without a separate select; `base` is that
@@ -356,6 +370,19 @@ __device__ __forceinline__ uint32_t scale_block_sum(uint32_t sum_bits, uint32_t 
 {
     uint32_t r;
     asm("v_fma_f32 %0, %1, %2, -%3" : "=v"(r) : "v"(sum_bits), "v"(q), "v"(Cb), "s"(tok));
+    return r;
+}
+
+// Where one lane holds the whole block sum, the sum accumulates from Cb's
+// bits instead: 2^q is the unit in the last place of Cb = 1.5 * 2^(E+10),
+// whose low 22 fraction bits are zero, so Cb's bits plus n (|n| < 2^21) are
+// the bits of Cb + n * 2^q, inside Cb's binade [2^(E+10), 2^(E+11)).  The
+// difference of two binary32 values in one binade is exact in any rounding
+// mode: one subtraction gives n * 2^q.
+__device__ __forceinline__ uint32_t sub_block_base(uint32_t sum_bits, uint32_t Cb, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_sub_f32 %0, %1, %2" : "=v"(r) : "v"(sum_bits), "v"(Cb), "s"(tok));
     return r;
 }
 
@@ -1019,6 +1046,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     // once per chain: with the incoming c's term, on the chain's first lane
     constexpr uint32_t SUM_BASE = CUT_EACH_BLOCK ? 0u : kSumBase;
     const uint32_t base_on = lane_g == 0 ? SUM_BASE : 0u;
+    // one lane per chain: the block sum starts from Cb instead (the epilogue
+    // is then one subtraction, see sub_block_base)
+    constexpr bool CB_BASE = !CUT_EACH_BLOCK && G == 1;
     uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -1167,7 +1197,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         // the hopper incoming-accumulator kernel: left out there)
                         if constexpr (!(CIN && BLK == 32)) asm("" : "+v"(cb));
                         Cb[i][j] = cb;
-                        acc[i][j] = c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE);
+                        acc[i][j] = CB_BASE ? c_block_term_cb(c[i][j], Cb[i][j], tok)
+                                            : c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             } else {
@@ -1229,8 +1260,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         asm("" : "+v"(cb));  // later uses derive from C itself
                         Cb[i][j] = cb;
                         // c enters the block sum once
-                        acc[i][j] = (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE)
-                                             : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi, base_on);
+                        acc[i][j] = CB_BASE  ? c_block_term_cb(c[i][j], Cb[i][j], tok)
+                                    : (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE)
+                                               : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi, base_on);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             }
@@ -1342,6 +1374,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                     if constexpr (CUT_EACH_BLOCK) {
                         const uint32_t tf = __float_as_uint((float)acc[i][j]);
                         cn = mul_exact(cut14(tf), Cb[i][j] - POW2Q_FROM_C, tok);
+                    } else if constexpr (CB_BASE) {
+                        cn = sub_block_base((uint32_t)acc[i][j], Cb[i][j], tok);
                     } else {
                         cn = scale_block_sum((uint32_t)acc[i][j], Cb[i][j] - POW2Q_FROM_C, Cb[i][j], tok);
                     }
