@@ -790,17 +790,23 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // Without the bound of 3 for 4x4 tiles the compiler gave the 64x64
 // matrix-core kernel of incoming accumulators 200 VGPRs (2 waves per SIMD),
 // which cost it 9% on 8192^3 (49.3 against 44.7 ms, A/B in one session).
-template <int RM, int RN>
+// 4x4 tiles of fast accumulation run 4 waves per SIMD (their LDS lets 4
+// workgroups share a CU): with the term loop unrolled under step barriers
+// they fit in 117 VGPRs without spills (8192^3 39.3-39.5 against 39.8 ms for
+// 3 waves with the loop rolled, A/B in one session; the unrolled loop at 3
+// waves measured 41.1 ms, and 4 waves with the rolled loop 0.5% slower than
+// 3).  Slow accumulation and incoming accumulators would spill at 4 waves
+// and keep 3.
+template <int RM, int RN, int ACC>
 struct WavesPerSimd {
-    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 16 || RM * RN == 2) ? 3 : 4;
+    static constexpr bool FOUR = RM * RN == 16 && ACC == 0;  // ACC_FAST
+    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 2 || (RM * RN == 16 && !FOUR)) ? 3 : 4;
 };
-// Most waves per SIMD the compiler may schedule for: 3 for 4x4 thread tiles
-// (their LDS would let 4 workgroups share a CU, and the compiler then cut the
-// 64x64 matrix-core kernel from 154 to 120 VGPRs, 0.5% slower on 8192^3, A/B
-// in one session), otherwise the hardware's 8.
-template <int RM, int RN>
+// Most waves per SIMD the compiler may schedule for: those 4x4 tiles' own
+// count, otherwise the hardware's 8.
+template <int RM, int RN, int ACC>
 struct MaxWavesPerSimd {
-    static constexpr int value = (RM * RN == 16) ? 3 : 8;
+    static constexpr int value = (RM * RN == 16) ? WavesPerSimd<RM, RN, ACC>::value : 8;
 };
 
 // G lanes share each output chain (G = 1, 2 or 4): lane g of a chain takes
@@ -832,7 +838,7 @@ constexpr int ACC_FAST = 0, ACC_SLOW = 1, ACC_SLOW_CHUNKS = 2, ACC_FAST_CIN = 3;
 
 template <int XF, int WF, int BM, int BN, int RM, int RN, int G, int ACC, bool MX, int BLK, int SS>
 __global__ __launch_bounds__((BM / RM) * (BN / RN) * G)
-__attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<RM, RN>::value))) void main_kernel(
+__attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPerSimd<RM, RN, ACC>::value))) void main_kernel(
     MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
@@ -859,6 +865,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
     // tile, whose four waves per SIMD would then spill registers (it keeps
     // an unroll of 2); none for larger thread tiles (registers).
     constexpr int PASS_UNROLL = (RM * RN > 4) ? 1 : (SS == 2 && RM * RN == 4) ? 2 : 8;
+    // The 4x4 tiles of 4 waves per SIMD (256-thread workgroups; the one-wave
+    // 16x64 tile's LDS leaves it at 2) unroll the term loop of a block as
+    // well, with a scheduling barrier after every step: each step keeps its
+    // own LDS reads (the register budget of the rolled loop), while every
+    // address becomes a base plus an immediate offset (no per-step address
+    // additions).
+    constexpr bool STEP_FENCE = WavesPerSimd<RM, RN, ACC>::FOUR && NT == 256;
+    constexpr int TERM_UNROLL = STEP_FENCE ? K4PL : PASS_UNROLL;
     // CIN: fast accumulation from incoming accumulators c_in instead of +0
     constexpr bool CIN = ACC == ACC_FAST_CIN;
     constexpr bool FAST = ACC == ACC_FAST || CIN, CHUNKS = ACC == ACC_SLOW_CHUNKS;
@@ -1284,7 +1298,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
 #pragma unroll
                 for (int j = 0; j < RN; ++j) bh4[j] = load_half_slice<K4PL>(wh + col_of(j) * AHS + 2 * k40);
             }
-#pragma unroll(PASS_UNROLL)
+#pragma unroll(TERM_UNROLL)
             for (int u = 0; u < K4PL; ++u) {
                 const int k4 = hb * (BLK / 4) + lane_g * K4PL + u;
                 float4 av[V16 ? 1 : RM], bv[V16 ? 1 : RN];
@@ -1351,6 +1365,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN>::value, MaxWavesPerSimd<
                         a = dot2_i16(__builtin_amdgcn_perm(r3, r2, 0x05040100u), sign_pair(sa[i].y, sb[j].y), a);
                         acc[i][j] = a;
                     }
+                if constexpr (STEP_FENCE) __builtin_amdgcn_sched_barrier(0);
             }
 
             if (G >= 2) {

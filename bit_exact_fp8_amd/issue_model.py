@@ -92,20 +92,23 @@ def target(ins: str):
 
 def stage_weights(blocks, inner_trips: int, then_share: float):
     """Per-stage execution weights of the stage loop's blocks: the loop is
-    the span from the first block holding an s_barrier that a later block
-    branches back to, up to the last such block; a block branching to
-    itself is the inner loop (inner_trips runs per stage); the sides of an
-    exec-mask if / else (a
-    block with s_xor_b64 of exec ending in s_cbranch_execz) weigh then_share
-    and 1 - then_share."""
+    the union of the backward branches (block j to an earlier or the same
+    block i) whose span i..j holds an s_barrier, from the smallest i to the
+    largest j (the compiler may rotate the loop so that it is entered in its
+    middle); a block branching to itself is the inner loop (inner_trips runs
+    per stage); the sides of an exec-mask if / else (a block with s_xor_b64
+    of exec ending in s_cbranch_execz) weigh then_share and 1 - then_share."""
     labels = [b[0] for b in blocks]
-
-    def back_edges(i):
-        return [j for j, b in enumerate(blocks) if j > i and any(
-            target(x) == labels[i] for x in b[1] if x.startswith(TERMINATORS))]
-
-    head = next(i for i, b in enumerate(blocks) if any(x.startswith("s_barrier") for x in b[1]) and back_edges(i))
-    latch = max(back_edges(head))
+    index = {lab: i for i, lab in enumerate(labels)}
+    barrier = [any(x.startswith("s_barrier") for x in b[1]) for b in blocks]
+    spans = []
+    for j, (_, ins) in enumerate(blocks):
+        for x in ins:
+            i = index.get(target(x)) if x.startswith(TERMINATORS) else None
+            if i is not None and i <= j and any(barrier[i:j + 1]):
+                spans.append((i, j))
+    head = min(i for i, _ in spans)
+    latch = max(j for _, j in spans)
     w = {}
     i = head
     while i <= latch:
