@@ -574,8 +574,11 @@ __device__ __forceinline__ void decode_chunk(uint4 raw, float *va, uint32_t *ve,
 }
 
 // decode_chunk with a binary16 value plane (8 words for the 16 codes).
-template <int FMT, uint32_t EBIAS>
-__device__ __forceinline__ void decode_chunk_h(uint4 raw, uint32_t *vh, uint32_t *ve, uint32_t *vs)
+// SWZ: each plane's 32 bytes for the chunk are two 16-byte blocks, stored
+// at word offsets o0 and 4 - o0 (o0 = 0 or 4, see the 4-lane tiles' row
+// swizzle in the kernel).
+template <int FMT, uint32_t EBIAS, bool SWZ = false>
+__device__ __forceinline__ void decode_chunk_h(uint4 raw, uint32_t *vh, uint32_t *ve, uint32_t *vs, int o0 = 0)
 {
     const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
     uint32_t h[8], ep[8], sp[8];
@@ -590,6 +593,16 @@ __device__ __forceinline__ void decode_chunk_h(uint4 raw, uint32_t *vh, uint32_t
         const uint32_t t = w << 8;
         sp[2 * q] = __builtin_amdgcn_perm(t, w, 0x08080A0Au);
         sp[2 * q + 1] = __builtin_amdgcn_perm(t, w, 0x09090B0Bu);
+    }
+    if constexpr (SWZ) {
+        const int o1 = 4 - o0;
+        *reinterpret_cast<uint4 *>(vh + o0) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4 *>(vh + o1) = make_uint4(h[4], h[5], h[6], h[7]);
+        *reinterpret_cast<uint4 *>(ve + o0) = make_uint4(ep[0], ep[1], ep[2], ep[3]);
+        *reinterpret_cast<uint4 *>(ve + o1) = make_uint4(ep[4], ep[5], ep[6], ep[7]);
+        *reinterpret_cast<uint4 *>(vs + o0) = make_uint4(sp[0], sp[1], sp[2], sp[3]);
+        *reinterpret_cast<uint4 *>(vs + o1) = make_uint4(sp[4], sp[5], sp[6], sp[7]);
+        return;
     }
     *reinterpret_cast<uint4 *>(vh) = make_uint4(h[0], h[1], h[2], h[3]);
     *reinterpret_cast<uint4 *>(vh + 4) = make_uint4(h[4], h[5], h[6], h[7]);
@@ -891,6 +904,17 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
     static_assert(!V16 || (G == 4 && K4PL <= 2 && !MX) || (G == 1 && MX), "binary16 value planes");
     constexpr int SST = sign_stride<G, BLK>();
     constexpr int XS = BM * SST, WS = BN * SST;
+    // 4-lane tiles with 32-product blocks: every plane row is 64 bytes, four
+    // 16-byte blocks, lane g of a chain reading block g.  The decode writes a
+    // chunk (half a row) as two 16-byte stores per plane, 8 lanes at a time
+    // from 4 consecutive rows: unswizzled, rows r and r + 2 put them on the
+    // same banks.  Storing block b of row r at b ^ ((r >> 1) & 1) spreads
+    // those 8 stores over all 32 banks, and every 8 lanes of a read (2 rows x
+    // 4 blocks) still cover them once.
+    constexpr bool SWZ = G == 4 && BLK == 32;
+    static_assert(!SWZ || (PST == KP && AHS == KP && SST == KP && SIGN16 && SLICE16 && NBS == 1),
+                  "swizzled 64-byte rows");
+    auto swz = [&](int row) { return SWZ ? 4 * ((row >> 1) & 1) : 0; };  // word offset
     constexpr int XPW = 4 * BM * PW_ROW, WPW = 4 * BN * PW_ROW;  // power-plane words per stage
 
     // LDS planes of SS consecutive stages (k-list positions pos .. pos + 32*SS)
@@ -1116,8 +1140,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                                                        xp + st * XPW + ((2 * half) * BM + r) * PW_ROW,
                                                        xp + st * XPW + ((2 * half + 1) * BM + r) * PW_ROW, r);
                     else if (V16)
-                        decode_chunk_h<XF, X_EBIAS>(raw[q], reinterpret_cast<uint32_t *>(xa) + r * AHS + 8 * half,
-                                                    xe + r * PST + 8 * half, xs + r * SST + 8 * half);
+                        decode_chunk_h<XF, X_EBIAS, SWZ>(raw[q], reinterpret_cast<uint32_t *>(xa) + r * AHS + 8 * half,
+                                                         xe + r * PST + 8 * half, xs + r * SST + 8 * half, swz(r));
                     else
                         decode_chunk<XF, X_EBIAS>(raw[q], xa + r * A_STRIDE + 16 * half,
                                                   xe + r * PST + 8 * half, xs + r * SST + 8 * half);
@@ -1138,8 +1162,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                                                        wp + st * WPW + ((2 * half) * BN + rw) * PW_ROW,
                                                        wp + st * WPW + ((2 * half + 1) * BN + rw) * PW_ROW, rw);
                     else if (V16)
-                        decode_chunk_h<WF, W_EBIAS>(raw[q], reinterpret_cast<uint32_t *>(wa) + rw * AHS + 8 * half,
-                                                    we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
+                        decode_chunk_h<WF, W_EBIAS, SWZ>(raw[q], reinterpret_cast<uint32_t *>(wa) + rw * AHS + 8 * half,
+                                                         we + rw * PST + 8 * half, wsg + rw * SST + 8 * half, swz(rw));
                     else
                         decode_chunk<WF, W_EBIAS>(raw[q], wa + rw * A_STRIDE + 16 * half,
                                                   we + rw * PST + 8 * half, wsg + rw * SST + 8 * half);
@@ -1228,10 +1252,10 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                         uint4 ea[RM], eb[RN];
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
-                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * PST + wo);
+                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * PST + (wo ^ swz(tm + i * TM)));
 #pragma unroll
                         for (int j = 0; j < RN; ++j)
-                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * PST + wo);
+                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * PST + (wo ^ swz(tn + j * TN)));
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -1294,9 +1318,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                 const uint32_t *xh = reinterpret_cast<const uint32_t *>(xa);
                 const uint32_t *wh = reinterpret_cast<const uint32_t *>(wa);
 #pragma unroll
-                for (int i = 0; i < RM; ++i) ah4[i] = load_half_slice<K4PL>(xh + row_of(i) * AHS + 2 * k40);
+                for (int i = 0; i < RM; ++i)
+                    ah4[i] = load_half_slice<K4PL>(xh + row_of(i) * AHS + ((2 * k40) ^ swz(row_of(i))));
 #pragma unroll
-                for (int j = 0; j < RN; ++j) bh4[j] = load_half_slice<K4PL>(wh + col_of(j) * AHS + 2 * k40);
+                for (int j = 0; j < RN; ++j)
+                    bh4[j] = load_half_slice<K4PL>(wh + col_of(j) * AHS + ((2 * k40) ^ swz(col_of(j))));
             }
 #pragma unroll(TERM_UNROLL)
             for (int u = 0; u < K4PL; ++u) {
@@ -1311,7 +1337,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                         ah2[i] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint32_t *>(xa) +
                                                                   row_of(i) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
-                        if ((u & 1) == 0) sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + 2 * k4);
+                        if ((u & 1) == 0)
+                            sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + ((2 * k4) ^ swz(row_of(i))));
                         sa[i] = (u & 1) ? make_uint2(sa4[i].z, sa4[i].w) : make_uint2(sa4[i].x, sa4[i].y);
                     } else {
                         sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * SST + 2 * k4);
@@ -1324,7 +1351,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                         bh2[j] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint32_t *>(wa) +
                                                                   col_of(j) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
-                        if ((u & 1) == 0) sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + 2 * k4);
+                        if ((u & 1) == 0)
+                            sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + ((2 * k4) ^ swz(col_of(j))));
                         sb[j] = (u & 1) ? make_uint2(sb4[j].z, sb4[j].w) : make_uint2(sb4[j].x, sb4[j].y);
                     } else {
                         sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * SST + 2 * k4);

@@ -49,6 +49,7 @@ constexpr int PER_ITER = 4 * CHAINS;  // instructions per loop iteration (op ker
     X(MED3_I32, "v_med3_i32", "v_med3_i32 %[a], %[a], -1, 1")                                                             \
     X(MAD_I32_I16, "v_mad_i32_i16", "v_mad_i32_i16 %[a], %[a], %[b], %[a]")                                               \
     X(MUL_F32, "v_mul_f32", "v_mul_f32 %[a], %[a], %[b]")                                                                 \
+    X(SUB_F32, "v_sub_f32", "v_sub_f32 %[a], %[a], %[b]")                                                                 \
     X(MUL_LO_U32, "v_mul_lo_u32", "v_mul_lo_u32 %[a], %[a], %[b]")                                                        \
     X(CNDMASK_B32, "v_cndmask_b32", "v_cndmask_b32 %[a], %[a], %[b], vcc")                                                \
     X(CMP_EQ_U32, "v_cmp_eq_u32", "v_cmp_eq_u32 vcc, %[a], %[b]")                                                         \
