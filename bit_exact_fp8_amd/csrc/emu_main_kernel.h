@@ -1085,8 +1085,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
     constexpr uint32_t SUM_BASE = CUT_EACH_BLOCK ? 0u : kSumBase;
     const uint32_t base_on = lane_g == 0 ? SUM_BASE : 0u;
     // one lane per chain: the block sum starts from Cb instead (the epilogue
-    // is then one subtraction, see sub_block_base)
-    constexpr bool CB_BASE = !CUT_EACH_BLOCK && G == 1;
+    // is then one subtraction, see sub_block_base; where c stays cut after
+    // every block, the cut follows it: n * 2^q is a normal binary32 value on
+    // every block whose result is used, biased E >= 94, so cutting it and
+    // cutting n before the scaling clear the same bits)
+    constexpr bool CB_BASE = G == 1;
     uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -1414,7 +1417,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
                     uint32_t cn;
-                    if constexpr (CUT_EACH_BLOCK) {
+                    if constexpr (CUT_EACH_BLOCK && CB_BASE) {
+                        cn = cut14(sub_block_base((uint32_t)acc[i][j], Cb[i][j], tok));
+                    } else if constexpr (CUT_EACH_BLOCK) {
                         const uint32_t tf = __float_as_uint((float)acc[i][j]);
                         cn = mul_exact(cut14(tf), Cb[i][j] - POW2Q_FROM_C, tok);
                     } else if constexpr (CB_BASE) {
