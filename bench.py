@@ -11,13 +11,13 @@ integer-VALU ceiling.
 roofline.peak (bound "alu") is the VALU issue ceiling of the path's term
 loop: every multiply-add needs one truncating FMA, and half of a byte
 permute, a sign-pair bitop and a 16-bit dot product (2.5 instructions per
-lane), and that mix issues at 3.42 cycles per wave instruction on gfx950
+lane), and that mix issues at 3.40 cycles per wave instruction on gfx950
 (measured, profiles/issue_ceiling.md), so the chip's 1,024 SIMDs at 2.4 GHz
-issue at most 1,024 x 2.4e9 / 3.42 x 64 / 2.5 multiply-adds per second:
-36.8e12 GEMM-ops/s.  Everything else the kernel issues (decode, block
+issue at most 1,024 x 2.4e9 / 3.40 x 64 / 2.5 multiply-adds per second:
+37.0e12 GEMM-ops/s.  Everything else the kernel issues (decode, block
 maxima, per-block prologue and epilogue, addressing) counts against it.
-roofline.issue_peak prices the kernel's own instructions (3.18 lane slots per
-multiply-add, counted in its assembly) at that rate: 29.0e12 GEMM-ops/s.
+roofline.issue_peak prices the kernel's own instructions (3.05 lane slots per
+multiply-add, counted in its assembly) at that rate: 30.3e12 GEMM-ops/s.
 roofline.frac_vs_R is the achieved rate over the survey's op-count model R,
 which charges 7 packed 16-bit integer operations per multiply-add (exponent
 add, block maximum, alignment distance, significand product, shift-truncate,
