@@ -18,7 +18,7 @@ issue at most 1,024 x 2.4e9 / 3.40 x 64 / 2.5 multiply-adds per second:
 maxima, per-block prologue and epilogue, addressing) counts against it.
 roofline.issue_peak prices the kernel's own instructions (3.05 lane slots per
 multiply-add, counted in its assembly) at that rate: 30.3e12 GEMM-ops/s.
-roofline.frac_vs_R is the achieved rate over the survey's op-count model R,
+roofline.frac_vs_R is the achieved rate over the op-count model R,
 which charges 7 packed 16-bit integer operations per multiply-add (exponent
 add, block maximum, alignment distance, significand product, shift-truncate,
 sign, accumulate): 256 x 64 x 2.4e9 x 2 / 7 x 2 = 22.47e12 GEMM-ops/s; the
@@ -51,7 +51,7 @@ from bit_exact_fp8_amd.inputs import (FP8_DTYPES, OUT_DTYPES, WORKLOADS, make_op
 SIMDS, CLOCK = 256 * 4, 2.4e9
 TERM_MIX_CYCLES = 3.38                     # cycles per wave instruction of the term mix (measured; see below)
 TERM_LOOP_SLOTS_PER_MAC = 2.5              # fma + (perm + bitop3 + dot2c) / 2
-R_MODEL = 256 * 64 * 2.4e9 * 2 / 7 * 2    # the survey's op-count model: 7 packed ops per MAC
+R_MODEL = 256 * 64 * 2.4e9 * 2 / 7 * 2    # op-count model R: 7 packed 16-bit ops per MAC at 16 lanes per clock
 METRIC = "bit-exact emulated FP8 GEMM ops/s (2MNK/s) and % of int-VALU roofline"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
