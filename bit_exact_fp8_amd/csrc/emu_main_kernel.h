@@ -810,10 +810,18 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // waves measured 41.1 ms, and 4 waves with the rolled loop 0.5% slower than
 // 3).  Slow accumulation and incoming accumulators would spill at 4 waves
 // and keep 3.
-template <int RM, int RN, int ACC>
+// The 4-lane tiles with 32-product blocks read their LDS words a stage ahead
+// into registers (see LDS_PF in the kernel); a 512-thread workgroup of them
+// is two waves per SIMD, the most their grids (one workgroup per CU) give,
+// so their bound is 2 (up to 256 VGPRs; a 1024-thread workgroup stays within
+// 128 by its size).
+template <int RM, int RN, int ACC, int G = 1, int BLK = 32>
 struct WavesPerSimd {
     static constexpr bool FOUR = RM * RN == 16 && ACC == 0;  // ACC_FAST
-    static constexpr int value = (RM * RN > 16) ? 2 : (RM * RN == 2 || (RM * RN == 16 && !FOUR)) ? 3 : 4;
+    static constexpr int value = (G == 4 && BLK == 32)                             ? 2
+                                 : (RM * RN > 16)                                  ? 2
+                                 : (RM * RN == 2 || (RM * RN == 16 && !FOUR)) ? 3
+                                                                                   : 4;
 };
 // Most waves per SIMD the compiler may schedule for: those 4x4 tiles' own
 // count, otherwise the hardware's 8.
@@ -851,7 +859,7 @@ constexpr int ACC_FAST = 0, ACC_SLOW = 1, ACC_SLOW_CHUNKS = 2, ACC_FAST_CIN = 3;
 
 template <int XF, int WF, int BM, int BN, int RM, int RN, int G, int ACC, bool MX, int BLK, int SS>
 __global__ __launch_bounds__((BM / RM) * (BN / RN) * G)
-__attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPerSimd<RM, RN, ACC>::value))) void main_kernel(
+__attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, MaxWavesPerSimd<RM, RN, ACC>::value))) void main_kernel(
     MainParams p)
 {
     static_assert(G == 1 || G == 2 || G == 4, "G lanes per chain: 1, 2 or 4");
@@ -952,6 +960,29 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
     const int64_t pos_end = RANGED ? ((pos_begin + span < sq.len) ? pos_begin + span : sq.len) : sq.len;
 
     for (int i = t; i < BM + BN + CHUNKS; i += NT) flags[i] = 0;
+
+    // The 4-lane tiles with 32-product blocks (one output per thread) read a
+    // stage's six 16-byte LDS words -- exponents, binary16 values and signs of
+    // the x and the w row, lane g's block g of each -- one stage ahead, into
+    // registers: the reads of stage st + 1 are in flight while stage st
+    // computes its chain.
+    constexpr bool LDS_PF = SWZ && RM == 1 && RN == 1;
+    struct StageReads {
+        uint4 ea, eb, ah, bh, sa, sb;
+    };
+    auto stage_reads = [&](int st) {
+        StageReads r;
+        const int ox = (4 * lane_g) ^ swz(tm), ow = (4 * lane_g) ^ swz(tn);
+        const uint32_t *xh = reinterpret_cast<const uint32_t *>(xa_all + st * XA);
+        const uint32_t *wh = reinterpret_cast<const uint32_t *>(wa_all + st * WA);
+        r.ea = *reinterpret_cast<const uint4 *>(xe_all + st * XP + tm * PST + ox);
+        r.eb = *reinterpret_cast<const uint4 *>(we_all + st * WP + tn * PST + ow);
+        r.ah = *reinterpret_cast<const uint4 *>(xh + tm * AHS + ox);
+        r.bh = *reinterpret_cast<const uint4 *>(wh + tn * AHS + ow);
+        r.sa = *reinterpret_cast<const uint4 *>(xs_all + st * XS + tm * SST + ox);
+        r.sb = *reinterpret_cast<const uint4 *>(wsg_all + st * WS + tn * SST + ow);
+        return r;
+    };
 
     uint32_t myflag[CPT];
     uint4 raw[CPT];
@@ -1177,6 +1208,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
         // prefetch the next stages; latency hidden by the compute below
         if (pos + (int64_t)KB * SS < pos_end) load_block(pos + (int64_t)KB * SS);
 
+        [[maybe_unused]] StageReads nxt;
+        if constexpr (LDS_PF) nxt = stage_reads(0);
         // all the stages of one barrier unrolled: every LDS address of the
         // stage's planes is then a per-thread base plus an immediate offset
         // (not for two stages of 2x2 thread tiles: unrolled, their four
@@ -1191,6 +1224,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
         // reads during the previous stage's arithmetic); slow accumulation
         // stops at the end (its chunk boundaries count positions).
         if (!FAST && spos >= pos_end) break;  // uniform across the workgroup
+        [[maybe_unused]] StageReads cur;
+        if constexpr (LDS_PF) {
+            cur = nxt;
+            if (st + 1 < SS) nxt = stage_reads(st + 1);
+        }
         const float *xa = xa_all + st * XA, *wa = wa_all + st * WA;
         const uint32_t *xe = xe_all + (MX ? 0 : st * XP), *we = we_all + (MX ? 0 : st * WP);
         const uint32_t *xs = xs_all + st * XS, *wsg = wsg_all + st * WS;
@@ -1253,12 +1291,19 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                 for (int wo = hb * WPB + lane_g * WPL; wo < hb * WPB + (lane_g + 1) * WPL; wo += WU) {
                     if constexpr (WU == 4) {
                         uint4 ea[RM], eb[RN];
+                        if constexpr (LDS_PF) {
+                            ea[0] = cur.ea;
+                            eb[0] = cur.eb;
+                        } else {
 #pragma unroll
-                        for (int i = 0; i < RM; ++i)
-                            ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * PST + (wo ^ swz(tm + i * TM)));
+                            for (int i = 0; i < RM; ++i)
+                                ea[i] = *reinterpret_cast<const uint4 *>(xe + (tm + i * TM) * PST +
+                                                                         (wo ^ swz(tm + i * TM)));
 #pragma unroll
-                        for (int j = 0; j < RN; ++j)
-                            eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * PST + (wo ^ swz(tn + j * TN)));
+                            for (int j = 0; j < RN; ++j)
+                                eb[j] = *reinterpret_cast<const uint4 *>(we + (tn + j * TN) * PST +
+                                                                         (wo ^ swz(tn + j * TN)));
+                        }
 #pragma unroll
                         for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -1316,7 +1361,10 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
             // binary16 values: the lane's whole slice of the block (K4PL steps
             // of 4 codes, 2 words each) in one read per row
             uint4 ah4[SLICE16 ? RM : 1], bh4[SLICE16 ? RN : 1];
-            if constexpr (SLICE16) {
+            if constexpr (LDS_PF) {
+                ah4[0] = cur.ah;
+                bh4[0] = cur.bh;
+            } else if constexpr (SLICE16) {
                 const int k40 = hb * (BLK / 4) + lane_g * K4PL;
                 const uint32_t *xh = reinterpret_cast<const uint32_t *>(xa);
                 const uint32_t *wh = reinterpret_cast<const uint32_t *>(wa);
@@ -1341,7 +1389,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                                                                   row_of(i) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0)
-                            sa4[i] = *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST + ((2 * k4) ^ swz(row_of(i))));
+                            sa4[i] = LDS_PF ? cur.sa
+                                            : *reinterpret_cast<const uint4 *>(xs + row_of(i) * SST +
+                                                                               ((2 * k4) ^ swz(row_of(i))));
                         sa[i] = (u & 1) ? make_uint2(sa4[i].z, sa4[i].w) : make_uint2(sa4[i].x, sa4[i].y);
                     } else {
                         sa[i] = *reinterpret_cast<const uint2 *>(xs + row_of(i) * SST + 2 * k4);
@@ -1355,7 +1405,9 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC>::value, MaxWavesPer
                                                                   col_of(j) * AHS + 2 * k4);
                     if constexpr (SIGN16) {
                         if ((u & 1) == 0)
-                            sb4[j] = *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST + ((2 * k4) ^ swz(col_of(j))));
+                            sb4[j] = LDS_PF ? cur.sb
+                                            : *reinterpret_cast<const uint4 *>(wsg + col_of(j) * SST +
+                                                                               ((2 * k4) ^ swz(col_of(j))));
                         sb[j] = (u & 1) ? make_uint2(sb4[j].z, sb4[j].w) : make_uint2(sb4[j].x, sb4[j].y);
                     } else {
                         sb[j] = *reinterpret_cast<const uint2 *>(wsg + col_of(j) * SST + 2 * k4);
