@@ -810,15 +810,15 @@ __device__ __forceinline__ void tile_order(int &tile_m, int &tile_n)
 // waves measured 41.1 ms, and 4 waves with the rolled loop 0.5% slower than
 // 3).  Slow accumulation and incoming accumulators would spill at 4 waves
 // and keep 3.
-// The 4-lane tiles with 32-product blocks read their LDS words a stage ahead
-// into registers (see LDS_PF in the kernel); a 512-thread workgroup of them
-// is two waves per SIMD, the most their grids (one workgroup per CU) give,
-// so their bound is 2 (up to 256 VGPRs; a 1024-thread workgroup stays within
-// 128 by its size).
+// The 4-lane tiles with 32-product blocks in fast accumulation read their
+// LDS words a stage ahead into registers (see LDS_PF in the kernel); a
+// 512-thread workgroup of them is two waves per SIMD, the most their grids
+// (one workgroup per CU) give, so their bound is 2 (up to 256 VGPRs; a
+// 1024-thread workgroup stays within 128 by its size).
 template <int RM, int RN, int ACC, int G = 1, int BLK = 32>
 struct WavesPerSimd {
     static constexpr bool FOUR = RM * RN == 16 && ACC == 0;  // ACC_FAST
-    static constexpr int value = (G == 4 && BLK == 32)                             ? 2
+    static constexpr int value = (G == 4 && BLK == 32 && (ACC == 0 || ACC == 3))   ? 2
                                  : (RM * RN > 16)                                  ? 2
                                  : (RM * RN == 2 || (RM * RN == 16 && !FOUR)) ? 3
                                                                                    : 4;
@@ -961,12 +961,12 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, Max
 
     for (int i = t; i < BM + BN + CHUNKS; i += NT) flags[i] = 0;
 
-    // The 4-lane tiles with 32-product blocks (one output per thread) read a
-    // stage's six 16-byte LDS words -- exponents, binary16 values and signs of
+    // The 4-lane tiles with 32-product blocks (one output per thread) in fast
+    // accumulation read a stage's six 16-byte LDS words -- exponents, binary16 values and signs of
     // the x and the w row, lane g's block g of each -- one stage ahead, into
     // registers: the reads of stage st + 1 are in flight while stage st
     // computes its chain.
-    constexpr bool LDS_PF = SWZ && RM == 1 && RN == 1;
+    constexpr bool LDS_PF = SWZ && RM == 1 && RN == 1 && FAST;
     struct StageReads {
         uint4 ea, eb, ah, bh, sa, sb;
     };
