@@ -112,8 +112,6 @@ constexpr uint32_t SUM_OFFSET = 0x400u;
 // (M << 23) drops M's bit 9 and above, so the 0x400 offset of the maximum
 // vanishes from C.
 constexpr uint32_t C_OFFSET = (10u << 23) | 0x400000u;
-// 2^q with q = E - 13 has exponent field (E + 127) - 13 = C's field - 23.
-constexpr uint32_t POW2Q_FROM_C = (23u << 23) | 0x400000u;
 
 // Exponent maximum on the matrix cores.  x codes become 2^(4*ex + 4), w codes
 // 2^(4*ew + 4), zeros 0 (bf16 "power planes"), so the product of a nonzero
@@ -306,31 +304,30 @@ __device__ __forceinline__ uint32_t fma_abs_rz_hi16(uint32_t a, uint32_t b, uint
     return r;
 }
 
+// The block sum starts from C's own bits: 2^q, the block's quantum, is the
+// unit in the last place of Cb = 1.5 * 2^(E+10), whose low 22 fraction bits
+// are zero, so Cb's bits plus the integer sum n (|n| < 2^21: at most 32
+// terms and c's, each below 2^15) are the bits of Cb + n * 2^q, inside Cb's
+// binade [2^(E+10), 2^(E+11)).  The difference of two binary32 values in one
+// binade is exact in any rounding mode: one subtraction gives n * 2^q.
+__device__ __forceinline__ uint32_t sub_block_base(uint32_t sum_bits, uint32_t Cb, uint32_t tok)
+{
+    uint32_t r;
+    asm("v_sub_f32 %0, %1, %2" : "=v"(r) : "v"(sum_bits), "v"(Cb), "s"(tok));
+    return r;
+}
+
 // The incoming accumulator's term of a block sum, in units of the block's
 // quantum: |c| cut toward zero by the RTZ fma against C (the low 16 bits of
 // the result, below 2^15), times c's sign: the sign from c's bits read as a
 // signed integer, clamped to [-1, 1] (-0 gives -1, which only multiplies a
 // zero magnitude), and a signed 16-bit multiply, in one statement so that no
-// wait is placed between its three dependent instructions; `base` is added
-// (the block sum's offset, see kSumBase).  (A form with the sign as the
+// wait is placed between its three dependent instructions; Cb's bits are
+// added, the sum's start (see sub_block_base).  (A form with the sign as the
 // 16-bit pair (+-1, 0) and a dot product takes one instruction more; on
 // MI355X it measured slower in every kernel once the LDS planes were free of
 // bank conflicts: 8192^3 hopper 43.4 against 42.3 ms.)
-__device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t tok, uint32_t base)
-{
-    int acc;
-    uint32_t sgn, r;
-    asm("v_med3_i32 %1, %3, -1, 1\n\t"
-        "v_fma_f32 %2, |%3|, 1.0, %4\n\t"
-        "v_mad_i32_i16 %0, %2, %1, %6"
-        : "=v"(acc), "=&v"(sgn), "=&v"(r)
-        : "v"(c), "v"(Cb), "s"(tok), "s"(base));
-    return acc;
-}
-
-// The same term with the block sum starting from Cb's own bits (see
-// sub_block_base): Cb is both the truncating addend and the sum's offset.
-__device__ __forceinline__ int c_block_term_cb(uint32_t c, uint32_t Cb, uint32_t tok)
+__device__ __forceinline__ int c_block_term(uint32_t c, uint32_t Cb, uint32_t tok)
 {
     int acc;
     uint32_t sgn, r;
@@ -344,8 +341,9 @@ __device__ __forceinline__ int c_block_term_cb(uint32_t c, uint32_t Cb, uint32_t
 
 // The same term where G lanes share a chain and it enters the block sum on
 // one lane only: that lane clamps c's bits to [lo, hi] = [-1, 1], the others
-// to [0, 0], so their term is 0 without a separate select; `base` is that
-// lane's offset (0 on the others).
+// to [0, 0], so their term is 0 without a separate select; `base` is Cb's
+// bits on that lane and 0 on the others, so that the chain's sum across its
+// lanes starts from Cb once.
 __device__ __forceinline__ int c_block_term_on(uint32_t c, uint32_t Cb, uint32_t tok, int lo, int hi, uint32_t base)
 {
     int acc;
@@ -356,43 +354,6 @@ __device__ __forceinline__ int c_block_term_on(uint32_t c, uint32_t Cb, uint32_t
         : "=v"(acc), "=&v"(sgn), "=&v"(r)
         : "v"(c), "v"(Cb), "s"(tok), "v"(lo), "v"(hi), "v"(base));
     return acc;
-}
-
-// The block sum n (|n| < 2^21: at most 32 terms and c's, each below 2^15)
-// accumulates from kSumBase, the bits of 1.5 * 2^23, so that its bits read as
-// a binary32 are exactly 1.5 * 2^23 + n.  Then, with Cb = 1.5 * 2^(E+10) =
-// 1.5 * 2^23 * 2^q and 2^q the block's quantum, fma(1.5 * 2^23 + n, 2^q, -Cb)
-// is n * 2^q exactly (at most 21 significant bits): the conversion and the
-// scaling in one instruction.
-constexpr uint32_t kSumBase = 0x4B400000u;
-
-__device__ __forceinline__ uint32_t scale_block_sum(uint32_t sum_bits, uint32_t q, uint32_t Cb, uint32_t tok)
-{
-    uint32_t r;
-    asm("v_fma_f32 %0, %1, %2, -%3" : "=v"(r) : "v"(sum_bits), "v"(q), "v"(Cb), "s"(tok));
-    return r;
-}
-
-// Where one lane holds the whole block sum, the sum accumulates from Cb's
-// bits instead: 2^q is the unit in the last place of Cb = 1.5 * 2^(E+10),
-// whose low 22 fraction bits are zero, so Cb's bits plus n (|n| < 2^21) are
-// the bits of Cb + n * 2^q, inside Cb's binade [2^(E+10), 2^(E+11)).  The
-// difference of two binary32 values in one binade is exact in any rounding
-// mode: one subtraction gives n * 2^q.
-__device__ __forceinline__ uint32_t sub_block_base(uint32_t sum_bits, uint32_t Cb, uint32_t tok)
-{
-    uint32_t r;
-    asm("v_sub_f32 %0, %1, %2" : "=v"(r) : "v"(sum_bits), "v"(Cb), "s"(tok));
-    return r;
-}
-
-// a * b where the product is exact (a power of two times a value of at most
-// 14 significant bits, in the normal range), in any mode.
-__device__ __forceinline__ uint32_t mul_exact(uint32_t a, uint32_t b, uint32_t tok)
-{
-    uint32_t r;
-    asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b), "s"(tok));
-    return r;
 }
 
 // a + b in the current (round-to-nearest-even) mode.
@@ -1111,16 +1072,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, Max
     // Incoming accumulators keep c cut after every block (they select c
     // itself on some blocks).
     constexpr bool CUT_EACH_BLOCK = CIN;
-    // the block sums' offset (kSumBase where the epilogue reads it), entered
-    // once per chain: with the incoming c's term, on the chain's first lane
-    constexpr uint32_t SUM_BASE = CUT_EACH_BLOCK ? 0u : kSumBase;
-    const uint32_t base_on = lane_g == 0 ? SUM_BASE : 0u;
-    // one lane per chain: the block sum starts from Cb instead (the epilogue
-    // is then one subtraction, see sub_block_base; where c stays cut after
-    // every block, the cut follows it: n * 2^q is a normal binary32 value on
-    // every block whose result is used, biased E >= 94, so cutting it and
-    // cutting n before the scaling clear the same bits)
-    constexpr bool CB_BASE = G == 1;
+    // The block sum starts from Cb's bits (the epilogue is then one
+    // subtraction, see sub_block_base; where c stays cut after every block,
+    // the cut follows it: n * 2^q is a normal binary32 value on every block
+    // whose result is used, biased E >= 94, so cutting it and cutting n
+    // before the scaling clear the same bits).  Where G lanes share a chain
+    // only its first lane adds Cb's bits (masked by cb_on), with the incoming
+    // c's term; the quad sums then give every lane of the chain Cb + n.
+    const uint32_t cb_on = lane_g == 0 ? 0xFFFFFFFFu : 0u;
     uint32_t slow[RUNNING ? RM : 1][RUNNING ? RN : 1];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
@@ -1276,8 +1235,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, Max
                         // the hopper incoming-accumulator kernel: left out there)
                         if constexpr (!(CIN && BLK == 32)) asm("" : "+v"(cb));
                         Cb[i][j] = cb;
-                        acc[i][j] = CB_BASE ? c_block_term_cb(c[i][j], Cb[i][j], tok)
-                                            : c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE);
+                        acc[i][j] = c_block_term(c[i][j], Cb[i][j], tok);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             } else {
@@ -1346,9 +1304,8 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, Max
                         asm("" : "+v"(cb));  // later uses derive from C itself
                         Cb[i][j] = cb;
                         // c enters the block sum once
-                        acc[i][j] = CB_BASE  ? c_block_term_cb(c[i][j], Cb[i][j], tok)
-                                    : (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok, SUM_BASE)
-                                               : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi, base_on);
+                        acc[i][j] = (G == 1) ? c_block_term(c[i][j], Cb[i][j], tok)
+                                             : c_block_term_on(c[i][j], Cb[i][j], tok, c_lo, c_hi, Cb[i][j] & cb_on);
                         if constexpr (CIN) c[i][j] = cut14(c[i][j]);
                     }
             }
@@ -1462,23 +1419,14 @@ __attribute__((amdgpu_waves_per_eu(WavesPerSimd<RM, RN, ACC, G, BLK>::value, Max
                     }
             }
 
-            // block epilogue: the exact sum scaled by 2^q (cut to 14 significant
-            // bits first where c must stay cut after every block)
+            // block epilogue: the exact sum scaled by 2^q (then cut to 14
+            // significant bits where c must stay cut after every block)
 #pragma unroll
             for (int i = 0; i < RM; ++i)
 #pragma unroll
                 for (int j = 0; j < RN; ++j) {
-                    uint32_t cn;
-                    if constexpr (CUT_EACH_BLOCK && CB_BASE) {
-                        cn = cut14(sub_block_base((uint32_t)acc[i][j], Cb[i][j], tok));
-                    } else if constexpr (CUT_EACH_BLOCK) {
-                        const uint32_t tf = __float_as_uint((float)acc[i][j]);
-                        cn = mul_exact(cut14(tf), Cb[i][j] - POW2Q_FROM_C, tok);
-                    } else if constexpr (CB_BASE) {
-                        cn = sub_block_base((uint32_t)acc[i][j], Cb[i][j], tok);
-                    } else {
-                        cn = scale_block_sum((uint32_t)acc[i][j], Cb[i][j] - POW2Q_FROM_C, Cb[i][j], tok);
-                    }
+                    uint32_t cn = sub_block_base((uint32_t)acc[i][j], Cb[i][j], tok);
+                    if constexpr (CUT_EACH_BLOCK) cn = cut14(cn);
                     if constexpr (CIN) {
                         // c (cut to 14 significant bits by the prologue) stays when
                         // the block exponent, biased, is below 94 -- no products
