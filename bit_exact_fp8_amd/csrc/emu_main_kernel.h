@@ -1576,21 +1576,33 @@ hipError_t launch_cfg(const MainParams &p, int S, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Stages per barrier for the 16x8 tile with 4 lanes per output: 16 halve the
-// barrier rounds of long k-lists (16 x 256 x 65536 with 8 splits: 0.0858
-// against 0.0923 ms, A/B in one session; 32 do not fit the 16-product blocks'
-// LDS), but in fast accumulation every stage of the last round is computed,
-// so the host counts one round as its stages plus about 1.3 stages of
-// barrier and decode overhead (from that measurement) and takes 16 where
-// that costs less for the longest split (8 for short k-lists such as K = 256).
-inline bool long_klist(const MainParams &p)
+// Stages per barrier for the 16x8 tile with 4 lanes per output.  Longer
+// rounds halve the barrier rounds of long k-lists (16 x 256 x 65536 with 8
+// splits: 16 stages 0.0858 against 0.0923 ms for 8, A/B in one session), but
+// in fast accumulation every stage of the last round is computed, so the
+// host counts one round as its stages plus about 1.3 stages of barrier and
+// decode overhead (from that measurement) and takes the round that costs
+// least for the longest split, the shorter on a tie.  32 stages fit the LDS
+// (144 KB) with 32-product blocks only, and there they also even out the
+// decode: 1,536 chunks per round, three for each of the 512 threads (16
+// stages give half of them two and the other half one).
+inline int g4_stages(const MainParams &p, int max_ss)
 {
     const int64_t W = int64_t(1) << p.tile_shift;
     const int64_t nt = (p.K + W - 1) >> p.tile_shift;
     const int64_t tiles = p.round_robin ? (nt + p.S - 1) / p.S : p.tps;
     const int64_t len = (tiles * W < p.K) ? tiles * W : p.K;
     const int64_t stages = (len + KB - 1) / KB;
-    return ((stages + 15) / 16) * (3 * 16 + 4) < ((stages + 7) / 8) * (3 * 8 + 4);
+    int best = 8;
+    int64_t best_cost = ((stages + 7) / 8) * (3 * 8 + 4);
+    for (int ss = 16; ss <= max_ss; ss *= 2) {
+        const int64_t cost = ((stages + ss - 1) / ss) * (3 * ss + 4);
+        if (cost < best_cost) {
+            best = ss;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 template <int XF, int WF, int BLK>
@@ -1606,8 +1618,10 @@ hipError_t launch_fmt(int cfg, const MainParams &p, int S, hipStream_t stream)
     case TILE_64x64_MX: return launch_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_64x128_MX: return launch_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, S, stream);
     case TILE_16x8_G4:
-        return long_klist(p) ? launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 16>(p, S, stream)
-                             : launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, S, stream);
+        if constexpr (BLK == 32)
+            if (g4_stages(p, 32) == 32) return launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 32>(p, S, stream);
+        return g4_stages(p, 16) == 16 ? launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 16>(p, S, stream)
+                                      : launch_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, S, stream);
     case TILE_16x64_MX: return launch_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, S, stream);
     case TILE_32x32_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, S, stream);
     case TILE_32x32_MX_S4: return launch_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, S, stream);
@@ -1650,8 +1664,8 @@ hipError_t launch_variant_cin(int cfg, const MainParams &p, hipStream_t stream)
     case TILE_64x64_MX: return launch_cin_cfg<XF, WF, 64, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_64x128_MX: return launch_cin_cfg<XF, WF, 64, 128, 4, 8, 1, true, BLK>(p, stream);
     case TILE_16x8_G4:
-        return long_klist(p) ? launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 16>(p, stream)
-                             : launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, stream);
+        return g4_stages(p, 16) == 16 ? launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 16>(p, stream)
+                                      : launch_cin_cfg<XF, WF, 16, 8, 1, 1, 4, false, BLK, 8>(p, stream);
     case TILE_16x64_MX: return launch_cin_cfg<XF, WF, 16, 64, 4, 4, 1, true, BLK>(p, stream);
     case TILE_32x32_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, false, BLK, 4>(p, stream);
     case TILE_32x32_MX_S4: return launch_cin_cfg<XF, WF, 32, 32, 2, 2, 1, true, BLK, 4>(p, stream);

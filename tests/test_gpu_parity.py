@@ -330,11 +330,13 @@ def test_stage_forms_of_the_32x32_tile(dev, orc, shape, forced):
 
 @pytest.mark.parametrize("profile", ["hopper", "ada-pairwise"])
 def test_16x8_tile_long_klists(dev, orc, profile):
-    """The 16x8 tile with 4 lanes per output stages 16 K-blocks per barrier
-    on long k-lists (8 on short ones): a ragged K whose last round is
-    partial (2960 = 92.5 stages of 32), fast and slow, unsplit and split
-    into k-lists of different lengths, NaN / Inf codes in one row, and chains
-    from incoming accumulators, against the oracle."""
+    """The 16x8 tile with 4 lanes per output stages 32 K-blocks per barrier
+    on long k-lists of 32-product blocks, 16 on those of 16-product blocks
+    and on shorter ones, and 8 on short ones: a ragged K whose last round is
+    partial (2960 = 92.5 stages of 32; 32 per round unsplit and over 3
+    splits, 16 over 2), fast and slow, unsplit and split into k-lists of
+    different lengths, NaN / Inf codes in one row, and chains from incoming
+    accumulators (at most 16 per round), against the oracle."""
     M, N, K = 17, 48, 2960
     gen = torch.Generator().manual_seed(2960)
     x = inject(random_codes((M, K), "e4m3fn", gen), "e4m3fn", 0.1, 0.05, gen)
