@@ -52,6 +52,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     if (!p.pairwise) {
         acc = split_partial(0);
         for (int s = 1; s < p.S; ++s) acc = acc + split_partial(s);
+    } else if (p.S <= 16) {
+        // The stride-halving tree itself, over 16 slots with fixed indices
+        // (registers): strides of S or more add nothing, so it is the tree
+        // over P for every S <= 16, each addition in the same order.
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = i < p.S ? split_partial(i) : 0.0f;
+#pragma unroll
+        for (int h = 8; h >= 1; h >>= 1)
+#pragma unroll
+            for (int i = 0; i < h; ++i)
+                if (i + h < p.S) v[i] = v[i] + v[i + h];
+        acc = v[0];
     } else {
         int L = 0;
         while ((1 << L) < p.S) ++L;
