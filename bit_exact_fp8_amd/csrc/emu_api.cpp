@@ -257,7 +257,7 @@ emu_status check_common(const uint8_t *x, emu_fp8_format xf, int64_t ldx, const 
 }
 
 // The combine kernel over S split partials (or chunk results) in `part`.
-emu_status launch_combine_of(const Plan &plan, const float *part, int S, int64_t M, int64_t N, int out_kind,
+emu_status launch_combine_of(const Plan &plan, float *part, int S, int64_t M, int64_t N, int out_kind,
                              void *out, int64_t ldo, const float *sx, const float *sw, const float *sr,
                              hipStream_t stream)
 {
@@ -363,7 +363,7 @@ emu_status run(const Plan &plan, const uint8_t *x, emu_fp8_format xf, int64_t ld
         if (e != hipSuccess) return fail(EMU_ERR_DEVICE, std::string("main kernel launch: ") + hipGetErrorString(e));
     }
     if (partials) {
-        emu_status st = launch_combine_of(plan, static_cast<const float *>(workspace), S, M, N, out_kind, out, ldo,
+        emu_status st = launch_combine_of(plan, static_cast<float *>(workspace), S, M, N, out_kind, out, ldo,
                                           sx, sw, sr, stream);
         if (st != EMU_OK) return st;
     }

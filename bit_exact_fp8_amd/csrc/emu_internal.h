@@ -90,7 +90,7 @@ struct DeferParams {
 };
 
 struct CombineParams {
-    const float *part;     // [S * cps, M, N] partials, dense
+    float *part;           // [S * cps, M, N] partials, dense (the pairwise tree over more than 16 splits runs in place)
     int S, M, N;
     int cps;               // partials per split: 1, or the slow-mode chunk results to add in order first
     int pairwise;          // 0: serial p0 + p1 + ...; 1: stride-halving pairwise tree

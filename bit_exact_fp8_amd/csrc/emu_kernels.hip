@@ -14,9 +14,8 @@ namespace {
 // the default round-to-nearest-even mode.  Serial: ((p0 + p1) + p2) + ...
 // Pairwise: the stride-halving tree over P = the next power of two >= S
 // (for h = P/2 .. 1: p_i += p_{i+h} where i + h < S; S = 3 gives
-// (p0 + p2) + p1).  That tree is the tree of adjacent pairs over the leaves
-// in bit-reversed index order, evaluated here left to right with one pending
-// left operand per level; leaves at index >= S are absent.  CHUNKED: the
+// (p0 + p2) + p1), run as that loop: in registers for S <= 16, in the
+// workspace beyond (no indexed local arrays, so no scratch memory).  CHUNKED: the
 // partials are slow-mode chunk results, cps per split (a separate kernel, so
 // that the one-partial-per-split case keeps its own simpler code).
 template <bool CHUNKED>
@@ -66,25 +65,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
                 if (i + h < p.S) v[i] = v[i] + v[i + h];
         acc = v[0];
     } else {
-        int L = 0;
-        while ((1 << L) < p.S) ++L;
-        float pend[17];
-        bool have[17];
-        for (int l = 0; l <= L; ++l) have[l] = false;
-        for (int j = 0; j < (1 << L); ++j) {
-            const int i = L ? (int)(__brev((unsigned)j) >> (32 - L)) : 0;
-            bool hv = i < p.S;
-            float v = hv ? split_partial(i) : 0.0f;
-            int l = 0;
-            for (int jj = j; jj & 1; jj >>= 1, ++l) {
-                if (have[l] && hv) v = pend[l] + v;
-                else if (have[l]) { v = pend[l]; hv = true; }
-                have[l] = false;
-            }
-            pend[l] = v;
-            have[l] = hv;
-        }
-        acc = pend[L];
+        // More splits: the same loop in place over this output's column of
+        // the workspace, each split's partial in its first slot (a stored
+        // chunk sum overwrites the split's first chunk after all of its
+        // chunks are read); every slot is read and written by this thread only.
+        float *q = p.part + idx;
+        const int64_t ss = (int64_t)p.cps * total;
+        if (CHUNKED)
+            for (int s = 0; s < p.S; ++s) q[s * ss] = split_partial(s);
+        int P = 1;
+        while (P < p.S) P <<= 1;
+        for (int h = P >> 1; h >= 1; h >>= 1)
+            for (int i = 0; i + h < p.S && i < h; ++i) q[i * ss] = q[i * ss] + q[(i + h) * ss];
+        acc = q[0];
     }
     uint32_t alpha = 0, sr = 0x3F800000u;
     if (p.out_kind != OUT_ACC_F32) {

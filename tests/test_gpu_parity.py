@@ -620,12 +620,15 @@ def test_rows_beyond_one_launch(dev, orc, S):
         assert_same(got, want, "incoming accumulators, rows beyond one launch")
 
 
-@pytest.mark.parametrize("profile", ["hopper", "ada-serial"])
+@pytest.mark.parametrize("profile", ["hopper", "ada-serial", "ada-pairwise"])
 @pytest.mark.parametrize("fast", [True, False])
 def test_largest_split_count(dev, orc, profile, fast):
     """split_S = 65535 (the largest grid z) on a K of three k-tiles: every
-    split after the third is empty and adds +0 in the serial combination, so
-    the result must equal the S = 3 one, which the oracle checks."""
+    split after the third is empty and adds +0 (partials are never -0), in
+    the serial combination and in the pairwise tree (whose strides of 2 and
+    1 then add p2 to p0 and p1 to that, as for S = 3; beyond 16 splits the
+    tree runs in place in the workspace), so the result must equal the S = 3
+    one, which the oracle checks."""
     tile = 128 if profile == "hopper" else 64
     M, N, K = 20, 32, 3 * tile
     gen = torch.Generator().manual_seed(73)
