@@ -160,7 +160,8 @@ typedef struct {
  * returns EMU_OK without enqueuing anything; K = 0 writes +0 everywhere.
  * workspace: device memory of emu_workspace_bytes(M, N, K, split_S,
  * fast_accum, profile, plan) bytes (may be NULL when that is 0), 4-byte
- * aligned; its contents on entry do not matter.  Only the split partials and
+ * aligned; its contents on entry do not matter and on return are
+ * unspecified (the combination may work in place).  Only the split partials and
  * stored chunk results are required (a smaller workspace returns
  * EMU_ERR_WORKSPACE); without the optional infinity lists at its end the
  * call is still bit-exact, only slower on large inputs whose e5m2 rows hold
