@@ -9,6 +9,10 @@ v0.1 documentation pages (user guide, FAQ, limitations, validation evidence):
   inputs, used to pin the C oracle (it also accepts an unbounded number of
   retained bits).
 
+Parity unpinned, as the header of ``emu_oracle.c`` lists: the canonical NaN
+bit patterns, the pairwise split tree for S >= 4 and the alignment of a
+subnormal incoming accumulator, which the pages leave open.
+
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never does, and this
 package imports nothing from it.

@@ -20,6 +20,16 @@
  * Readings taken where the pages are silent are marked "Reading:" and are
  * listed in the design notes of the repository.
  *
+ * Parity unpinned (nothing on the pages fixes these, so no test can pin
+ * them to more than this file's own reading): the canonical NaN bits of
+ * binary32, binary16 and bfloat16 outputs (0x7FFFFFFF, 0x7FFF) and of FP8
+ * outputs (0x7F); the pairwise split combination for S >= 4 (the pages fix
+ * only S = 3; the stride-halving tree is taken); the alignment of a
+ * subnormal incoming accumulator at binary32's emin.  The infinity and NaN
+ * outcomes of products and incoming accumulators follow IEEE arithmetic,
+ * which the tests pin, not the pages.  No result here is pinned to
+ * recordings of the reference hardware.
+ *
  * Mutants.  Building with -DORACLE_MUTANT=n (n > 0) plants one deliberate
  * mistake, so that the tests can show that their pins catch it.  The default
  * build (ORACLE_MUTANT 0) is the oracle.
